@@ -1,0 +1,202 @@
+"""Python face of the exact-attention oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  The product path (the HIP library and
+its binding) never imports it.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, IEEE double, OpenMP over
+query rows).  This wrapper only marshals numpy arrays into that library:
+
+* ``attention``   -- O and LSE by the naive definition (page "FlashAttention
+  (DE)", systems-analysis.info, section "Problematik der Standard-Attention")
+  or by the online-softmax recurrence (same page, section
+  "Online-Softmax-Berechnung") when ``block_keys > 0``;
+* ``probs_row``   -- one materialised row of P;
+* ``decode``      -- the oracle's own bfloat16 / OCP-E4M3 decoders.
+
+Inputs are the exact bytes the GPU receives: ``uint16`` arrays holding
+bfloat16 bit patterns, ``uint8`` arrays holding E4M3 codes (plus per-tensor
+scales), or ``float64`` arrays for hand-made cases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+DTYPES = {"bf16": 0, "e4m3": 1, "f64": 2}
+_NP = {"bf16": np.uint16, "e4m3": np.uint8, "f64": np.float64}
+
+_default = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle C source into a shared library with gcc (IEEE semantics)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+class OracleLib:
+    """One loaded copy of the oracle library (the default one, or a test's mutant)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)
+        lib.oracle_attention.restype = ctypes.c_int
+        lib.oracle_attention.argtypes = [vp, vp, vp, ctypes.c_int, dp, i64, i64, i64, i64, i64,
+                                         i64, ctypes.c_int, ctypes.c_double, ctypes.POINTER(i64),
+                                         i64, i64, dp, dp]
+        lib.oracle_probs_row.restype = ctypes.c_int
+        lib.oracle_probs_row.argtypes = [vp, vp, vp, ctypes.c_int, dp, i64, i64, i64, i64, i64,
+                                         i64, ctypes.c_int, ctypes.c_double, i64, dp]
+        lib.oracle_decode.restype = None
+        lib.oracle_decode.argtypes = [vp, ctypes.c_int, ctypes.c_double, i64, dp]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        self.lib = lib
+        self.path = path
+
+    def attention(self, q, k, v, *, causal, scale, dtype="bf16", descale=None, rows=None,
+                  block_keys=0):
+        return _attention(self.lib, q, k, v, causal, scale, dtype, descale, rows, block_keys)
+
+    def probs_row(self, q, k, v, *, causal, scale, row, dtype="bf16", descale=None):
+        return _probs_row(self.lib, q, k, v, causal, scale, row, dtype, descale)
+
+    def decode(self, codes, dtype, descale=1.0):
+        return _decode(self.lib, codes, dtype, descale)
+
+    def num_threads(self):
+        return int(self.lib.oracle_num_threads())
+
+
+def default() -> OracleLib:
+    """The oracle built from attn_oracle.c (rebuilt when the source is newer)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        _default = OracleLib(_LIB_PATH)
+    return _default
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _prep(q, k, v, dtype):
+    want = _NP[dtype]
+    arrs = []
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        t = np.ascontiguousarray(t)
+        if t.dtype != want:
+            raise TypeError(f"{name}: expected {np.dtype(want)} for dtype {dtype}, got {t.dtype}")
+        if t.ndim != 4:
+            raise ValueError(f"{name}: expected [B, H, N, d], got shape {t.shape}")
+        arrs.append(t)
+    q, k, v = arrs
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    return q, k, v, (B, Hq, Hkv, Nq, Nk, d)
+
+
+def _descale(dtype, descale):
+    if dtype != "e4m3":
+        return None
+    if descale is None or len(descale) != 3:
+        raise ValueError("e4m3 inputs need descale = (dq, dk, dv)")
+    return np.ascontiguousarray(np.asarray(descale, dtype=np.float64))
+
+
+def _attention(lib, q, k, v, causal, scale, dtype, descale, rows, block_keys):
+    """Return (O, LSE) in float64.
+
+    Without ``rows`` the shapes are O [B,Hq,Nq,d] and LSE [B,Hq,Nq]; with
+    ``rows`` (flat indices (b*Hq + h)*Nq + i) they are [n,d] and [n].
+    """
+    q, k, v, (B, Hq, Hkv, Nq, Nk, d) = _prep(q, k, v, dtype)
+    ds = _descale(dtype, descale)
+    if rows is None:
+        n = B * Hq * Nq
+        rows_arr, rows_ptr = None, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rows_arr.size
+        rows_ptr = rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    o = np.zeros((max(n, 1), d), dtype=np.float64)
+    lse = np.zeros(max(n, 1), dtype=np.float64)
+    rc = lib.oracle_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPES[dtype],
+                              _dptr(ds) if ds is not None else None,
+                              B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                              rows_ptr, n, int(block_keys), _dptr(o), _dptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_attention rejected its arguments")
+    o, lse = o[:n], lse[:n]
+    if rows is None:
+        return o.reshape(B, Hq, Nq, d), lse.reshape(B, Hq, Nq)
+    return o, lse
+
+
+def _probs_row(lib, q, k, v, causal, scale, row, dtype, descale):
+    q, k, v, (B, Hq, Hkv, Nq, Nk, d) = _prep(q, k, v, dtype)
+    ds = _descale(dtype, descale)
+    p = np.zeros(max(Nk, 1), dtype=np.float64)
+    rc = lib.oracle_probs_row(q.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPES[dtype],
+                              _dptr(ds) if ds is not None else None,
+                              B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                              int(row), _dptr(p))
+    if rc < 0:
+        raise ValueError("oracle_probs_row rejected its arguments")
+    return p[:Nk]
+
+
+def _decode(lib, codes, dtype, descale):
+    codes = np.ascontiguousarray(codes)
+    if codes.dtype != _NP[dtype]:
+        raise TypeError(f"expected {np.dtype(_NP[dtype])} codes for {dtype}")
+    out = np.empty(codes.size, dtype=np.float64)
+    lib.oracle_decode(codes.ctypes.data, DTYPES[dtype], float(descale), codes.size, _dptr(out))
+    return out.reshape(codes.shape)
+
+
+def attention(q, k, v, *, causal: bool, scale: float, dtype: str = "bf16", descale=None,
+              rows=None, block_keys: int = 0):
+    """Return (O, LSE) in float64.
+
+    Without ``rows`` the shapes are O [B,Hq,Nq,d] and LSE [B,Hq,Nq]; with
+    ``rows`` (flat indices (b*Hq + h)*Nq + i) they are [n,d] and [n].
+    ``block_keys == 0`` is the naive definition; ``> 0`` the online-softmax
+    recurrence over blocks of that many keys.
+    """
+    return default().attention(q, k, v, causal=causal, scale=scale, dtype=dtype,
+                               descale=descale, rows=rows, block_keys=block_keys)
+
+
+def probs_row(q, k, v, *, causal: bool, scale: float, row: int, dtype: str = "bf16",
+              descale=None):
+    """The materialised probability row P[row, :] (length Nk) in float64."""
+    return default().probs_row(q, k, v, causal=causal, scale=scale, row=row, dtype=dtype,
+                               descale=descale)
+
+
+def decode(codes: np.ndarray, dtype: str, descale: float = 1.0) -> np.ndarray:
+    """Decode bfloat16 bit patterns or E4M3 codes to float64 with the oracle's decoders."""
+    return default().decode(codes, dtype, descale)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle will use (OMP_NUM_THREADS, else all cores)."""
+    return default().num_threads()

@@ -1,0 +1,78 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant is a copy of the oracle's C source with one plausible mistake --
+a dropped term, a wrong sign, a wrong index, a swapped operand, a wrong
+constant -- compiled into a temporary library.  The pins of
+``oracle_pins.py`` are run against it, and at least one must fail.  This is
+evidence that the pins constrain every part of the oracle, not a check of
+the oracle itself.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle.oracle import _SRC, OracleLib, build
+from oracle_pins import PINS
+
+MUTANTS = {
+    "max_not_subtracted_in_lse": ("s[j] = exp(s[j] - M); L += s[j];", "s[j] = exp(s[j]); L += s[j];"),
+    "wrong_sign_in_exp": ("s[j] = exp(s[j] - M); L += s[j];", "s[j] = exp(M - s[j]); L += s[j];"),
+    "scale_dropped": ("s[j] = p->scale * dot;", "s[j] = dot;"),
+    "causal_off_by_one": ("return !p->causal || j <= i + (p->Nk - p->Nq);",
+                          "return !p->causal || j < i + (p->Nk - p->Nq);"),
+    "causal_top_left": ("return !p->causal || j <= i + (p->Nk - p->Nq);",
+                        "return !p->causal || j <= i;"),
+    "causal_transposed": ("return !p->causal || j <= i + (p->Nk - p->Nq);",
+                          "return !p->causal || j >= i + (p->Nk - p->Nq);"),
+    "gqa_interleaved": ("int64_t kvh = h / (p->Hq / p->Hkv);\n    int64_t qoff",
+                        "int64_t kvh = h % p->Hkv;\n    int64_t qoff"),
+    "lse_without_log": ("*lse = M + log(L);", "*lse = M + L;"),
+    "not_normalised": ("for (int64_t j = 0; j < p->Nk; ++j) s[j] /= L;                          /* s now holds P_j */",
+                       ""),
+    "v_replaced_by_k": ("o[t] += s[j] * load_elem(p->v,", "o[t] += s[j] * load_elem(p->k,"),
+    "v_row_index_wrong": ("int64_t voff = ((b * p->Hkv + kvh) * p->Nk + j) * p->d;\n        for (int64_t t = 0; t < p->d; ++t) o[t] += s[j]",
+                          "int64_t voff = ((b * p->Hkv + kvh) * p->Nk + (p->Nk - 1 - j)) * p->d;\n        for (int64_t t = 0; t < p->d; ++t) o[t] += s[j]"),
+    "q_k_dims_transposed": ("dot += qrow[t] * load_elem(p->k, p->dtype, koff + t, p->dk);",
+                            "dot += qrow[t] * load_elem(p->k, p->dtype, koff + (p->d - 1 - t), p->dk);"),
+    "empty_row_lse_zero": ("        *lse = -INFINITY;\n        return;\n    }\n    double L = 0.0;",
+                           "        *lse = 0.0;\n        return;\n    }\n    double L = 0.0;"),
+    "bf16_shift_wrong": ("uint32_t bits = ((uint32_t)h) << 16;", "uint32_t bits = ((uint32_t)h) << 15;"),
+    "e4m3_bias_wrong": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);", "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "e4m3_subnormal_wrong": ("mag = ldexp((double)m / 8.0, 1 - 7);", "mag = ldexp((double)m / 8.0, -7);"),
+    "descale_dropped": ("return oracle_e4m3_to_f64(((const uint8_t*)base)[idx]) * descale;",
+                        "return oracle_e4m3_to_f64(((const uint8_t*)base)[idx]);"),
+    "descale_q_k_swapped": ("p.dq = descale[0]; p.dk = descale[1]; p.dv = descale[2];\n    }\n    int64_t total",
+                            "p.dq = descale[0]; p.dk = descale[2]; p.dv = descale[1];\n    }\n    int64_t total"),
+    "tiled_alpha_not_applied_to_l": ("        l *= alpha;\n", ""),
+    "tiled_alpha_not_applied_to_o": ("        for (int64_t t = 0; t < p->d; ++t) o[t] *= alpha;\n", ""),
+    "tiled_last_block_dropped": ("int64_t j1 = j0 + Bc < p->Nk ? j0 + Bc : p->Nk;",
+                                 "int64_t j1 = j0 + Bc < p->Nk ? j0 + Bc : j0;"),
+    "probs_not_normalised": ("for (int64_t j = 0; j < Nk; ++j) prow[j] /= L;", ""),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(src.replace(old, new))
+    lib_path = build(force=True, src=str(path), out=str(tmp_path / f"libmut_{name}.so"))
+    mut = OracleLib(lib_path)
+    failures = []
+    for pin in PINS:
+        try:
+            pin(mut)
+        except AssertionError as e:   # the pin caught the planted mistake
+            failures.append(pin.__name__)
+        except (ValueError, FloatingPointError):
+            failures.append(pin.__name__)
+    assert failures, f"mutant {name} passed every pin"
+
+
+def test_unmutated_source_passes_every_pin():
+    orc = oracle.default()
+    for pin in PINS:
+        pin(orc)
