@@ -1,0 +1,173 @@
+#!/usr/bin/env python3
+"""Attention forward throughput on one MI355X.
+
+One step = one call of the fused attention forward (fa_fwd, one kernel
+launch) over the whole workload, inputs resident in device memory.  The
+default workload is the long-context causal configuration (B=2, H=16,
+N=16384, d=128, bf16, causal); ``--config`` selects another one.
+
+Prints one JSON line with the throughput in TFLOP/s (attention FLOPs
+4*B*Hq*Nq*Nk*d, halved for causal square problems), a ``roofline`` object
+for the kernel (MFMA-bound: achieved TFLOP/s against the dense MFMA peak of
+the input dtype; HBM-bound decode: algorithmic GB/s against 8 TB/s) and a
+``cpu_baseline`` object: the fp64 oracle timed on this host's cores on a
+bounded sample of rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}   # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOP/s on 1 MI355X (bf16/fp8) and % of MFMA peak"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(cfg_name: str, launches_bytes: float):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, x, budget_s: float):
+    """Time the oracle on sampled rows of the workload for about budget_s seconds."""
+    import oracle
+    rng = np.random.default_rng(12345)
+    total_rows = cfg.B * cfg.Hq * cfg.Nq
+    threads = oracle.num_threads()
+    # calibrate on a small batch, then run one batch sized to the budget
+    n0 = min(total_rows, max(8, threads * 2))
+    rows = np.sort(rng.choice(total_rows, size=n0, replace=False))
+    t0 = time.perf_counter()
+    oracle.attention(x["q"], x["k"], x["v"], causal=cfg.causal, scale=cfg.scale, dtype=cfg.dtype,
+                     descale=x.get("descale"), rows=rows)
+    dt0 = time.perf_counter() - t0
+    n = int(min(total_rows, max(n0, n0 * max(budget_s - dt0, 0.0) / max(dt0, 1e-6))))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.attention(x["q"], x["k"], x["v"], causal=cfg.causal, scale=cfg.scale, dtype=cfg.dtype,
+                     descale=x.get("descale"), rows=rows)
+    dt = time.perf_counter() - t0
+    i = rows % cfg.Nq
+    vis = np.minimum(cfg.Nk, i + (cfg.Nk - cfg.Nq) + 1) if cfg.causal else np.full(rows.shape, cfg.Nk)
+    vis = np.maximum(vis, 0)
+    # the metric's FLOP convention: 4*d per visible (query, key) pair, with the
+    # causal square problem counted at half the full-matrix work
+    flops = 4.0 * cfg.d * float(vis.sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} uniformly sampled query rows of {cfg.name} ({n / total_rows:.2%} of the rows, "
+                      f"{flops / 1e9:.1f} GFLOP by the visible-key count) in {dt:.1f} s, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long16k_causal")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the cpu_baseline leg (0 to skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from exact_attention_105_amd import fwd, load
+    from synth.inputs import CONFIGS, generate
+
+    load()
+    cfg = CONFIGS[args.config]
+    x = generate(cfg)
+    dev = torch.device("cuda:0")
+    if cfg.dtype == "bf16":
+        conv = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        conv = lambda a: torch.from_numpy(a).to(dev).view(torch.float8_e4m3fn)
+    q, k, v = conv(x["q"]), conv(x["k"]), conv(x["v"])
+    out = torch.empty((cfg.B, cfg.Hq, cfg.Nq, cfg.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((cfg.B, cfg.Hq, cfg.Nq), dtype=torch.float32, device=dev)
+    descale = x.get("descale")
+
+    def step():
+        fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, descale=descale, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms = ms_total / args.steps
+    tflops = cfg.flops / (ms * 1e-3) / 1e12
+
+    hbm_bound = cfg.Nq == 1
+    if hbm_bound:
+        gbs = cfg.algorithmic_bytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS}
+    else:
+        peak = PEAK_TFLOPS[cfg.dtype]
+        roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                "frac": tflops / peak}
+    roof["traffic"] = load_traffic(cfg.name, cfg.algorithmic_bytes)
+    roof["kernel_ms"] = ms
+
+    result = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) inputs)",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Nq": cfg.Nq,
+                   "Nk": cfg.Nk, "d": cfg.d, "causal": cfg.causal, "flops_per_step": cfg.flops,
+                   "algorithmic_bytes_per_step": cfg.algorithmic_bytes,
+                   "kernel_source_hash": kernel_source_hash()},
+        "roofline": roof,
+        "wall_s_timed": wall,
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

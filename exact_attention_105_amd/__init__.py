@@ -1,0 +1,9 @@
+"""Fused exact-attention forward pass for AMD MI355X (gfx950), HIP kernels behind a C ABI.
+
+``fwd(q, k, v, causal=..., scale=..., descale=...) -> (O, LSE)`` computes
+softmax(scale * Q K^T + mask) V and the per-row log-sum-exp in one kernel
+that never writes the score matrix to device memory.  The C ABI is declared
+in include/fa.h; ``_lib`` is its ctypes binding.
+"""
+from ._lib import EXPORTED, FaError, load, status_string, version  # noqa: F401
+from .attention import fwd  # noqa: F401

@@ -1,0 +1,86 @@
+"""ctypes binding of libfa.so (the C ABI declared in include/fa.h).
+
+Argument marshalling only: every step of the attention computation runs in
+the HIP kernels behind ``fa_fwd``.  There is no CPU fallback: if the library
+is missing or a call fails, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_DTYPE_BF16 = 0
+FA_DTYPE_FP8_E4M3 = 1
+
+FA_SUCCESS = 0
+FA_ERROR_INVALID_VALUE = 1
+FA_ERROR_NOT_SUPPORTED = 2
+FA_ERROR_LAUNCH_FAILURE = 3
+
+# every symbol include/fa.h declares
+EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_status_string", "fa_version")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_attention_105_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, fp, vp]
+    lib.fa_fwd_validate.restype = i32
+    lib.fa_fwd_validate.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, fp]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_version.restype = i32
+    lib.fa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _descale_arg(descale):
+    if descale is None:
+        return None
+    arr = (ctypes.c_float * 3)(*[float(x) for x in descale])
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), arr
+
+
+def fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype,
+           descale, stream) -> int:
+    """Raw call of fa_fwd with integer device pointers; returns the status code."""
+    ds = _descale_arg(descale)
+    return load().fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, int(causal),
+                         float(scale), int(dtype), ds[0] if ds else None, stream)
+
+
+def fa_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                    dtype, descale) -> int:
+    """Raw call of fa_fwd_validate (pure host function); returns the status code."""
+    ds = _descale_arg(descale)
+    return load().fa_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d,
+                                  int(causal), float(scale), int(dtype), ds[0] if ds else None)
+
+
+def version() -> int:
+    return load().fa_version()

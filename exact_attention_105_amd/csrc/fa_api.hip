@@ -1,0 +1,102 @@
+// C ABI of the attention forward library: argument validation and dispatch.
+// The contract of every entry point is documented in include/fa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace
+
+extern "C" fa_status_t fa_fwd_validate(const void* q, const void* k, const void* v, const void* o,
+                                       const float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                                       int d, int causal, float scale, fa_dtype_t dtype,
+                                       const float* descale_qkv) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || d < 1) return FA_ERROR_INVALID_VALUE;
+    if (Hq % Hkv != 0) return FA_ERROR_INVALID_VALUE;
+    if (causal != 0 && causal != 1) return FA_ERROR_INVALID_VALUE;
+    if (!isfinite(scale)) return FA_ERROR_INVALID_VALUE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3) return FA_ERROR_INVALID_VALUE;
+    if (dtype == FA_DTYPE_BF16 && descale_qkv != nullptr) return FA_ERROR_INVALID_VALUE;
+    if (dtype == FA_DTYPE_FP8_E4M3) {
+        if (descale_qkv == nullptr) return FA_ERROR_INVALID_VALUE;
+        for (int i = 0; i < 3; ++i)
+            if (!isfinite(descale_qkv[i]) || !(descale_qkv[i] > 0.f)) return FA_ERROR_INVALID_VALUE;
+    }
+    const int64_t q_elems = (int64_t)B * Hq * Nq * d;
+    const int64_t kv_elems = (int64_t)B * Hkv * Nk * d;
+    if (q_elems > kMaxElems || kv_elems > kMaxElems) return FA_ERROR_INVALID_VALUE;
+    const int64_t rows = (int64_t)B * Hq * Nq;
+    if (rows > 0) {
+        if (q == nullptr || o == nullptr) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(q, 16) || !aligned(o, 16)) return FA_ERROR_INVALID_VALUE;
+        if (lse != nullptr && !aligned(lse, 4)) return FA_ERROR_INVALID_VALUE;
+        if (kv_elems > 0) {
+            if (k == nullptr || v == nullptr) return FA_ERROR_INVALID_VALUE;
+            if (!aligned(k, 16) || !aligned(v, 16)) return FA_ERROR_INVALID_VALUE;
+        }
+    }
+    if (dtype == FA_DTYPE_BF16 && d != 64 && d != 128) return FA_ERROR_NOT_SUPPORTED;
+    if (dtype == FA_DTYPE_FP8_E4M3 && d != 128) return FA_ERROR_NOT_SUPPORTED;
+    return FA_SUCCESS;
+}
+
+extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                              float scale, fa_dtype_t dtype, const float* descale_qkv,
+                              hipStream_t stream) {
+    const fa_status_t st = fa_fwd_validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                                           dtype, descale_qkv);
+    if (st != FA_SUCCESS) return st;
+    if ((int64_t)B * Hq * Nq == 0) return FA_SUCCESS;
+
+    fa::FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.group = Hq / Hkv;
+    p.n_heads = B * Hq;
+    p.causal_shift = Nk - Nq;
+    // A negative scale is applied by flipping the sign bit of every Q
+    // element on load (exact in both formats) and using |scale|.
+    const float mag = fabsf(scale);
+    const bool neg = scale < 0.f;
+    if (dtype == FA_DTYPE_BF16) {
+        p.c = mag * fa::kLog2e;
+        p.o_scale = 1.f;
+        p.q_sign = neg ? 0x80008000u : 0u;
+    } else {
+        p.c = mag * descale_qkv[0] * descale_qkv[1] * fa::kLog2e;
+        p.o_scale = descale_qkv[2];
+        p.q_sign = neg ? 0x80808080u : 0u;
+    }
+
+    hipError_t err = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(p, d, causal != 0, stream)
+                                              : fa::launch_fwd_fp8(p, d, causal != 0, stream);
+    return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
+}
+
+extern "C" const char* fa_status_string(fa_status_t status) {
+    switch (status) {
+        case FA_SUCCESS: return "FA_SUCCESS: no error";
+        case FA_ERROR_INVALID_VALUE: return "FA_ERROR_INVALID_VALUE: an argument is outside its documented range";
+        case FA_ERROR_NOT_SUPPORTED: return "FA_ERROR_NOT_SUPPORTED: no kernel for this head dim / dtype combination";
+        case FA_ERROR_LAUNCH_FAILURE: return "FA_ERROR_LAUNCH_FAILURE: the HIP runtime rejected the kernel launch";
+    }
+    return "unknown fa_status_t";
+}
+
+extern "C" int fa_version(void) { return 100; }

@@ -1,0 +1,99 @@
+// Device-side building blocks of the attention forward kernels (gfx950 / CDNA4).
+//
+// Wave64 throughout.  The matrix products use the gfx950 MFMA instructions
+//   v_mfma_f32_32x32x16_bf16      (bf16 in, fp32 accumulate)
+//   v_mfma_f32_32x32x64_f8f6f4    (fp8 e4m3 in, fp32 accumulate)
+// whose 32x32 fp32 result is spread over the wave as: lane l holds column
+// n = l % 32 and rows 8*(i/4) + 4*(l/32) + (i%4) for its 16 accumulator
+// registers i = 0..15.  Both kernels put the query index on the column (n)
+// side, so every lane owns exactly one query row and the row statistics of
+// the online softmax live in that lane (and its partner lane l ^ 32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, Nq, Nk;
+    int group;          // Hq / Hkv
+    int n_qtiles;       // ceil(Nq / rows per workgroup)
+    int n_heads;        // B * Hq
+    int causal_shift;   // Nk - Nq: key j visible to query i iff j <= i + causal_shift
+    float c;            // |scale| (* sq * sk for fp8) * log2(e): exponent of 2 per raw score
+    float o_scale;      // multiplies the normalised output (sv * 2^-8 for fp8, 1 for bf16)
+    uint32_t q_sign;    // XOR mask applied to Q bit patterns (flips the sign when scale < 0)
+};
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp8 e4m3 x e4m3 (format code 0 for both operands), 32 bytes per lane per operand.
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Value of `x` combined over the lane pair (l, l ^ 32) with v_permlane32_swap.
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp32 values to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    bf16x2 r = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 16-byte global load / store through plain vector pointers.
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ void lds_store16(char* base, uint32_t off, u32x4 v) {
+    *reinterpret_cast<u32x4*>(base + off) = v;
+}
+__device__ __forceinline__ void lds_store8(char* base, uint32_t off, u32x2 v) {
+    *reinterpret_cast<u32x2*>(base + off) = v;
+}
+__device__ __forceinline__ u32x4 lds_load16(const char* base, uint32_t off) {
+    return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+// Heads are enumerated so that the Hq/Hkv query heads sharing one key/value
+// head get flat indices that are congruent modulo 8 whenever B*Hkv is a
+// multiple of 8; the hardware hands workgroups to the 8 XCDs round-robin, so
+// those heads (and their K/V traffic) land on the same XCD and its L2.
+__device__ __forceinline__ void head_of(const FwdParams& p, int x, int& b, int& hq, int& hkv) {
+    const int kvflat = x % (p.B * p.Hkv);
+    const int gi = x / (p.B * p.Hkv);
+    b = kvflat / p.Hkv;
+    hkv = kvflat % p.Hkv;
+    hq = hkv * p.group + gi;
+}
+
+}  // namespace fa

@@ -1,0 +1,16 @@
+// Internal launch entry points of the attention kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fa_device.hpp"
+
+namespace fa {
+
+// bf16 inputs, head dim 64 or 128.  Fills n_qtiles itself.
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
+
+// fp8 e4m3 inputs, head dim 128.  Fills n_qtiles itself.
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,106 @@
+/*
+ * fa.h -- C ABI of the fused exact-attention forward pass for AMD MI355X (gfx950).
+ *
+ * The library computes, for every batch b, query head h and query row i,
+ *
+ *     O[b,h,i,:] = sum_j P_ij V[b,kv(h),j,:],   P_ij = softmax_j(scale * <Q[b,h,i,:], K[b,kv(h),j,:]> + mask_ij)
+ *     LSE[b,h,i] = ln sum_j exp(scale * <Q[b,h,i,:], K[b,kv(h),j,:]> + mask_ij)
+ *
+ * i.e. exact scaled-dot-product attention (page "FlashAttention (DE)",
+ * systems-analysis.info, section "Problematik der Standard-Attention", the
+ * attention formula; exactness: page "Flash Attention", 21medien.de, key
+ * techniques), computed by one fused kernel that tiles Q and K/V, keeps a
+ * running row maximum and a running sum of exponentials per query row (same
+ * "FlashAttention (DE)" page, sections "Tiling und blockweise Verarbeitung"
+ * and "Online-Softmax-Berechnung") and never writes the N x N score matrix to
+ * device memory (same page, section "Zusammenfassen von Operationen in einem
+ * CUDA-Kernel").  The per-row log-sum-exp is the statistic a recomputing
+ * backward pass needs (page "Flash Attention", 21medien.de, overview:
+ * recomputation in the backward pass).
+ *
+ * Conventions that the pages leave open:
+ *  - causal masking (page "Flash Attention", 21medien.de, key techniques) is
+ *    aligned to the bottom-right corner: key j is visible to query i iff
+ *    j <= i + (Nk - Nq).  A row that sees no key gets O = 0 and LSE = -inf.
+ *  - grouped-query / multi-query attention (same page, key techniques): the
+ *    query head h reads key/value head kv(h) = h / (Hq / Hkv), i.e.
+ *    consecutive groups of Hq/Hkv query heads share one key/value head.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <hip/hip_runtime_api.h>  /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K and V.  O is always bfloat16, LSE always float32. */
+typedef enum {
+    FA_DTYPE_BF16 = 0,       /* bfloat16 (upper half of an IEEE binary32) */
+    FA_DTYPE_FP8_E4M3 = 1    /* OCP FP8 E4M3 (bias 7, max 448, no inf), per-tensor scales */
+} fa_dtype_t;
+
+typedef enum {
+    FA_SUCCESS = 0,
+    FA_ERROR_INVALID_VALUE = 1,   /* an argument is out of its documented range */
+    FA_ERROR_NOT_SUPPORTED = 2,   /* a valid combination this library has no kernel for */
+    FA_ERROR_LAUNCH_FAILURE = 3   /* the HIP runtime reported an error at launch */
+} fa_status_t;
+
+/*
+ * fa_fwd -- attention forward pass, asynchronous on `stream`.
+ *
+ * Pointers (all device memory, owned by the caller, 16-byte aligned,
+ * row-major and contiguous):
+ *   q    [B, Hq,  Nq, d]  elements of `dtype`
+ *   k    [B, Hkv, Nk, d]  elements of `dtype`
+ *   v    [B, Hkv, Nk, d]  elements of `dtype`
+ *   o    [B, Hq,  Nq, d]  bfloat16 output (written)
+ *   lse  [B, Hq,  Nq]     float32 output, natural-log log-sum-exp of the
+ *                         scaled, masked scores (written); may be NULL when
+ *                         the caller does not need it.
+ * Sizes: B >= 0, Hq >= 1, Hkv >= 1 with Hq % Hkv == 0, Nq >= 0, Nk >= 0,
+ *   d in {64, 128} for bf16 and d == 128 for fp8; every tensor must hold
+ *   fewer than 2^31 elements.  Nk == 0 makes every row see no key.
+ * causal: 0 or 1 (bottom-right aligned mask, see above).
+ * scale: multiplies the raw dot products; any finite value (callers
+ *   normally pass 1/sqrt(d), the formula's 1/sqrt(d_k)).
+ * descale_qkv: for FA_DTYPE_FP8_E4M3, a HOST pointer to three positive,
+ *   finite float32 values {sq, sk, sv}: the real inputs are code * s.  Must
+ *   be NULL for FA_DTYPE_BF16.
+ *
+ * Returns FA_SUCCESS after the kernel is enqueued (or when B*Hq*Nq == 0, in
+ * which case nothing is launched).  On any error nothing is launched and
+ * the outputs are untouched.  The library allocates no device memory and
+ * keeps no mutable global state; concurrent calls on different streams are
+ * safe.  The call does not synchronise; the caller orders later work on
+ * `stream` (or synchronises) before reading o and lse.
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   int causal, float scale, fa_dtype_t dtype,
+                   const float* descale_qkv, hipStream_t stream);
+
+/*
+ * fa_fwd_validate -- the argument checks fa_fwd performs before launching,
+ * as a pure host function (it makes no HIP call and touches no memory
+ * behind the pointers).  Returns the status fa_fwd would return for these
+ * arguments short of a launch failure.
+ */
+fa_status_t fa_fwd_validate(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                            int causal, float scale, fa_dtype_t dtype,
+                            const float* descale_qkv);
+
+/* A static, human-readable description of a status code. */
+const char* fa_status_string(fa_status_t status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

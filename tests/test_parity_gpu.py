@@ -1,0 +1,160 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small problems are compared element by element over the whole output; the
+full-size workloads are compared on sampled rows that the oracle computes
+one by one, plus properties that hold at any size.  Tolerances are in
+gpu_util.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_105_amd import FaError, fwd
+from gpu_util import (compare_bf16, oracle_ref, run_gpu, sample_rows, say, to_device)
+from synth.inputs import CONFIGS, generate, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import exact_attention_105_amd as fa
+    fa.load()
+
+
+# (B, Hq, Hkv, Nq, Nk, d, causal): several tiles, ragged tails, GQA/MQA,
+# Nq != Nk in both directions (bottom-right causal), single key, decode rows.
+SMALL = [
+    (1, 2, 2, 128, 128, 64, False),
+    (2, 3, 3, 300, 300, 64, True),
+    (2, 3, 3, 300, 300, 128, False),
+    (1, 4, 2, 257, 257, 128, True),
+    (2, 4, 1, 200, 333, 64, True),
+    (1, 2, 2, 333, 200, 128, True),
+    (1, 2, 2, 333, 200, 64, False),
+    (1, 2, 2, 129, 1, 64, False),
+    (1, 2, 2, 129, 1, 128, True),
+    (3, 8, 2, 1, 1000, 128, True),
+    (2, 8, 8, 1, 77, 64, False),
+    (1, 1, 1, 1, 1, 64, False),
+    (1, 2, 2, 64, 64, 128, True),
+    (1, 2, 2, 65, 65, 64, True),
+    (2, 2, 2, 190, 70, 64, False),
+    (1, 3, 1, 512, 512, 128, True),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}Nq{s[3]}Nk{s[4]}d{s[5]}{'c' if s[6] else 'n'}"
+                                               for s in SMALL])
+def test_small_bf16(shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    say(f"case {shape}")
+    x = make_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", 1000 + sum(shape))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_gpu(x, "bf16", causal, scale)
+    o_ref, lse_ref = oracle_ref(x, "bf16", causal, scale)
+    compare_bf16(o, lse, o_ref, lse_ref, str(shape))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 2.0, 1e-3])
+def test_scale_values(scale):
+    x = make_inputs(1, 2, 2, 150, 150, 64, "bf16", 31)
+    for causal in (False, True):
+        o, lse = run_gpu(x, "bf16", causal, scale)
+        o_ref, lse_ref = oracle_ref(x, "bf16", causal, scale)
+        compare_bf16(o, lse, o_ref, lse_ref, f"scale={scale} causal={causal}")
+
+
+def test_hand_cases_padded():
+    """The hand-worked 2x2 / 3x3 cases, zero-padded to d = 64 (padding leaves scores unchanged)."""
+    from oracle_pins import _scalar, load_hand_cases
+    from synth.inputs import f32_to_bf16_bits
+    for case in load_hand_cases():
+        n = len(case["q"])
+        pad = lambda vals: np.pad(np.array([_scalar(t) for t in vals], dtype=np.float32).reshape(1, 1, n, 1),
+                                  ((0, 0), (0, 0), (0, 0), (0, 63)))
+        x = {"q": f32_to_bf16_bits(pad(case["q"])), "k": f32_to_bf16_bits(pad(case["k"])),
+             "v": f32_to_bf16_bits(pad(case["v"]))}
+        for causal in (False, True):
+            o, lse = run_gpu(x, "bf16", causal, 1.0)
+            o_ref, lse_ref = oracle_ref(x, "bf16", causal, 1.0)
+            compare_bf16(o, lse, o_ref, lse_ref, f"{case['name']} causal={causal}")
+            key = "causal" if causal else "non_causal"
+            want = np.array([_scalar(t) for t in case[key]["o"]])
+            # bf16 inputs (ln 2, ln 3 rounded) and bf16 output keep O near the closed form
+            assert np.abs(o[0, 0, :, 0] - want).max() < 0.1
+            assert np.all(o[0, 0, :, 1:] == 0.0)
+
+
+def test_no_keys_and_no_queries():
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 2, 5, 64, device=dev).bfloat16()
+    k = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
+    o, lse = fwd(q, k, k.clone(), causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    q0 = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
+    kk = torch.randn(1, 2, 7, 64, device=dev).bfloat16()
+    o, lse = fwd(q0, kk, kk.clone(), causal=True)
+    assert o.shape == (1, 2, 0, 64)
+
+
+def test_errors_leave_outputs_untouched():
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 2, 8, 96, device=dev).bfloat16()
+    out = torch.full((1, 2, 8, 96), 7.0, device=dev, dtype=torch.bfloat16)
+    lse = torch.full((1, 2, 8), 7.0, device=dev)
+    with pytest.raises(FaError) as e:
+        fwd(q, q.clone(), q.clone(), out=out, lse=lse)
+    assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(lse == 7.0)
+
+
+def test_deterministic():
+    x = make_inputs(2, 4, 2, 700, 700, 128, "bf16", 77)
+    a = run_gpu(x, "bf16", True, 0.088)
+    b = run_gpu(x, "bf16", True, 0.088)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_lse_optional():
+    x = make_inputs(1, 2, 2, 100, 100, 64, "bf16", 78)
+    q, k, v = to_device(x, "bf16")
+    o1, l1 = fwd(q, k, v, causal=True)
+    o2, l2 = fwd(q, k, v, causal=True, return_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------------ full-size workloads
+BF16_CONFIGS = ["tiny", "gpt2", "gpt2_causal", "long16k_causal", "gqa_causal", "gqa_decode"]
+
+
+@pytest.mark.parametrize("name", BF16_CONFIGS)
+def test_config_bf16(name):
+    cfg = CONFIGS[name]
+    say(f"config {name}: {cfg}")
+    x = generate(cfg)
+    o, lse = run_gpu(x, "bf16", cfg.causal, cfg.scale)
+    assert np.all(np.isfinite(o)), "unwritten or non-finite outputs"
+    assert np.all(np.isfinite(lse))
+    rows_total = cfg.B * cfg.Hq * cfg.Nq
+    if rows_total <= 4096:
+        o_ref, lse_ref = oracle_ref(x, "bf16", cfg.causal, cfg.scale)
+        compare_bf16(o, lse, o_ref, lse_ref, name)
+    else:
+        rows = sample_rows(cfg.B, cfg.Hq, cfg.Nq, seed=cfg.seed)
+        o_ref, lse_ref = oracle_ref(x, "bf16", cfg.causal, cfg.scale, rows=rows)
+        compare_bf16(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
+                     f"{name} ({rows.size} sampled rows)")
+    if cfg.causal and cfg.Nq == cfg.Nk:
+        # row 0 sees only key 0: O_0 = V_0 exactly, for every head
+        from oracle_pins import bf16_to_f64_torch
+        v0 = bf16_to_f64_torch(x["v"][:, :, 0, :]).numpy()            # [B, Hkv, d]
+        g = cfg.Hq // cfg.Hkv
+        assert np.array_equal(o[:, :, 0, :], np.repeat(v0, g, axis=1))
