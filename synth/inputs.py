@@ -176,12 +176,15 @@ def make_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed, *, outlier_mult: float = 20.
                 "v": f32_to_bf16_bits(vf), "descale": None}
     if dtype != "e4m3":
         raise ValueError(f"unknown dtype {dtype}")
-    if Hq != Hkv:
-        raise ValueError("the E4M3 recipe marks channels of one head layout; use Hq == Hkv")
-    ch = outlier_channels(seed, Hq, d)
+    # outlier channels are drawn over the key/value heads; a query head gets
+    # the channels of the key/value head it reads (the same set when Hq == Hkv)
+    ch = outlier_channels(seed, Hkv, d)
     hs, ts = ch // d, ch % d
-    for t in (qf, kf, vf):
+    g = Hq // Hkv
+    for t in (kf, vf):
         t[:, hs, :, ts] *= np.float32(outlier_mult)
+    for gi in range(g):
+        qf[:, hs * g + gi, :, ts] *= np.float32(outlier_mult)
     qc, sq = quantise_e4m3(qf)
     kc, sk = quantise_e4m3(kf)
     vc, sv = quantise_e4m3(vf)

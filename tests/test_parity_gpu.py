@@ -158,3 +158,50 @@ def test_config_bf16(name):
         v0 = bf16_to_f64_torch(x["v"][:, :, 0, :]).numpy()            # [B, Hkv, d]
         g = cfg.Hq // cfg.Hkv
         assert np.array_equal(o[:, :, 0, :], np.repeat(v0, g, axis=1))
+
+
+# ------------------------------------------------------------------ FP8 (E4M3)
+FP8_SMALL = [
+    (1, 2, 2, 128, 128, False),
+    (2, 3, 3, 300, 300, True),
+    (1, 4, 2, 257, 190, True),
+    (1, 2, 2, 190, 257, False),
+    (2, 8, 2, 1, 700, True),
+    (1, 2, 2, 100, 1, False),
+]
+
+
+@pytest.mark.parametrize("shape", FP8_SMALL, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}Nq{s[3]}Nk{s[4]}{'c' if s[5] else 'n'}"
+                                                  for s in FP8_SMALL])
+def test_small_fp8(shape):
+    from gpu_util import compare_fp8
+    B, Hq, Hkv, Nq, Nk, causal = shape
+    say(f"fp8 case {shape}")
+    x = make_inputs(B, Hq, Hkv, Nq, Nk, 128, "e4m3", 2000 + sum(shape))
+    scale = 1.0 / math.sqrt(128)
+    o, lse = run_gpu(x, "e4m3", causal, scale)
+    o_ref, lse_ref = oracle_ref(x, "e4m3", causal, scale)
+    compare_fp8(o, lse, o_ref, lse_ref, f"fp8 {shape}")
+    # rows without any visible key follow the convention exactly
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref))
+
+
+def test_fp8_negative_scale():
+    from gpu_util import compare_fp8
+    x = make_inputs(1, 2, 2, 150, 150, 128, "e4m3", 2100)
+    o, lse = run_gpu(x, "e4m3", True, -0.05)
+    o_ref, lse_ref = oracle_ref(x, "e4m3", True, -0.05)
+    compare_fp8(o, lse, o_ref, lse_ref, "fp8 scale=-0.05")
+
+
+def test_config_fp8():
+    from gpu_util import compare_fp8
+    cfg = CONFIGS["fp8"]
+    say(f"config fp8: {cfg}")
+    x = generate(cfg)
+    o, lse = run_gpu(x, "e4m3", cfg.causal, cfg.scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = sample_rows(cfg.B, cfg.Hq, cfg.Nq, seed=cfg.seed)
+    o_ref, lse_ref = oracle_ref(x, "e4m3", cfg.causal, cfg.scale, rows=rows)
+    compare_fp8(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
+                f"fp8 ({rows.size} sampled rows)")
