@@ -86,6 +86,25 @@ def cpu_baseline(cfg, x, budget_s: float):
                       f"{flops / 1e9:.1f} GFLOP by the visible-key count) in {dt:.1f} s, fp64"}
 
 
+def copy_calibration(args):
+    """A plain device-to-device copy of a known size, timed like a step."""
+    import torch
+    n = args.copy_bytes // 4
+    src = torch.arange(n, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    # an elementwise kernel: reads n*4 bytes, writes n*4 bytes
+    for _ in range(args.warmup):
+        torch.add(src, 1, out=dst)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        torch.add(src, 1, out=dst)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(args.steps, 1)
+    print(json.dumps({"copy_bytes": n * 4, "steps": args.steps, "ms_per_copy": dt * 1e3,
+                      "GB_per_s": 2 * n * 4 / dt / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,7 +113,13 @@ def main():
     ap.add_argument("--config", default="long16k_causal")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 to skip)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of attention, run a plain device copy of this many bytes "
+                         "(calibrates the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_bytes > 0:
+        copy_calibration(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))

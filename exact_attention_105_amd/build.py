@@ -33,16 +33,22 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source for gfx950 and link libfa.so.  Returns its path."""
-    objdir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, jobs: int = 4, extra_flags=(), out: str = LIB,
+          objdir: str | None = None) -> str:
+    """Compile every source for gfx950 and link the library (libfa.so by default).
+
+    ``extra_flags`` are appended to every hipcc compile (e.g. -D tuning macros);
+    ``out``/``objdir`` place a variant build elsewhere.  Returns the library path.
+    """
+    objdir = objdir or os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     procs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
@@ -50,11 +56,11 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         if len(procs) >= jobs:
             _drain(procs)
     _drain(procs)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def _drain(procs):

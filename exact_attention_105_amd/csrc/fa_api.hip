@@ -1,5 +1,6 @@
 // C ABI of the attention forward library: argument validation and dispatch.
 // The contract of every entry point is documented in include/fa.h.
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -83,6 +84,12 @@ extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void*
         p.o_scale = descale_qkv[2];
         p.q_sign = neg ? 0x80808080u : 0u;
     }
+
+    // The kernels mask scores with -inf and rely on exp2(-inf * c) = 0, which
+    // needs c > 0.  A zero (or underflowing) scale uses the smallest normal
+    // float instead: every visible score times it rounds away against the
+    // exponent reference, so the weights stay exactly uniform.
+    p.c = fmaxf(p.c, FLT_MIN);
 
     hipError_t err = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(p, d, causal != 0, stream)
                                               : fa::launch_fwd_fp8(p, d, causal != 0, stream);

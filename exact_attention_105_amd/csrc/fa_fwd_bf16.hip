@@ -1,16 +1,17 @@
 // Fused exact-attention forward pass, bfloat16 inputs, head dim 64 or 128, gfx950.
 //
-// One workgroup owns BM = 128 query rows of one (batch, query head) and
+// One workgroup owns BM = 256 query rows of one (batch, query head) and
 // streams the key/value rows of that head's key/value head through LDS in
 // tiles of BN = 64 keys ("FlashAttention (DE)", systems-analysis.info,
 // section "Tiling und blockweise Verarbeitung").  Each of the four waves owns
-// 32 query rows and keeps, per row, a running maximum and a running sum of
+// 64 query rows and keeps, per row, a running maximum and a running sum of
 // exponentials (same page, section "Online-Softmax-Berechnung"); scores,
 // mask, softmax and the product with V never leave the chip (same page,
 // section "Zusammenfassen von Operationen in einem CUDA-Kernel").  Only O and
 // the per-row log-sum-exp are written.
 //
-// Matrix layout (gfx950 MFMA 32x32x16 bf16, see fa_device.hpp):
+// Matrix layout (gfx950 MFMA 32x32x16 bf16, see fa_device.hpp), per wave and
+// per 32-query block qb of its 64 rows:
 //   S^T = K Q^T    : A = K rows from LDS (ds_read_b128), B = Q rows held in
 //                    registers for the whole key loop.  Lane l ends up with
 //                    the scores of query l%32 against 16 of every 32 keys.
@@ -18,16 +19,18 @@
 //                    transposing read ds_read_b64_tr_b16 (16 lanes read a
 //                    4-key x 16-d block; each lane receives one d column of
 //                    4 keys), B = P straight from the score registers.
-// So P never touches LDS and V is never transposed in memory.
+// Every K and V^T fragment read from LDS feeds two MFMAs (the wave's two
+// query blocks), which halves LDS traffic per flop against 32 rows per wave;
+// with 32 rows per wave the LDS reads alone take about as long as the MFMAs.
 //
 // K/V staging: the global loads go straight into LDS (global_load_lds_dwordx4,
-// 1 KiB per wave instruction, no staging registers).  LDS rows are XOR
-// swizzled in 16-byte units -- by the row index for K, so the 32 rows a
-// ds_read_b128 touches hit distinct banks, and by 2*(row%4) for V, so the
-// four rows one transposing read touches do -- and the swizzle is realised
-// by choosing which global 16 bytes each lane fetches.  Two LDS stages: the
-// loads of tile j+1 are issued right after the barrier that publishes tile
-// j and land while tile j is computed.
+// 1 KiB per wave instruction, no staging registers), NSTAGE tiles deep.  LDS
+// rows are XOR swizzled in 16-byte units -- K by (row mod 16) (mod 8 at
+// d = 64), so the rows one ds_read_b128 touches hit distinct banks, V by
+// 2*(row mod 4), so the four rows one transposing read touches do -- and the
+// swizzle is realised by choosing which global 16 bytes each lane fetches.
+// All per-lane LDS and global offsets are loop invariant; a tile only adds
+// scalar bases.
 //
 // Online softmax with a lazily updated reference: the exponent reference of
 // a row only moves when its running maximum exceeds the reference by more
@@ -44,41 +47,55 @@ namespace fa {
 
 constexpr float kRescaleLog2 = 8.0f;
 
+#ifndef FA_BF16_RW128
+#define FA_BF16_RW128 32     // query rows per wave at d = 128 (32 or 64)
+#endif
+#ifndef FA_BF16_RW64
+#define FA_BF16_RW64 32      // query rows per wave at d = 64 (32 or 64)
+#endif
+#ifndef FA_BF16_NSTAGE
+#define FA_BF16_NSTAGE 2     // K/V tiles resident in LDS (2 or 3)
+#endif
+
 template <int D>
 struct Bf16Cfg {
     static constexpr int NW = 4;                 // waves per workgroup
-    static constexpr int BM = 32 * NW;           // query rows per workgroup
+    static constexpr int RW = D == 128 ? FA_BF16_RW128 : FA_BF16_RW64;  // query rows per wave
+    static constexpr int NQB = RW / 32;          // 32-row query blocks per wave
+    static constexpr int BM = RW * NW;           // query rows per workgroup
     static constexpr int BN = 64;                // keys per K/V tile
+    static constexpr int NSTAGE = FA_BF16_NSTAGE;
+    static constexpr int OCC = RW == 32 ? 2 : 1; // workgroups per CU the registers allow
     static constexpr int ROW = D * 2;            // bytes of one K or V row in LDS
     static constexpr int UPR = D / 8;            // 16-byte units per row
     static constexpr int TILE = BN * ROW;        // bytes of one K (or V) tile
     static constexpr int STAGE = 2 * TILE;       // K tile + V tile
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int LDS = NSTAGE * STAGE > BM * ROW ? NSTAGE * STAGE : BM * ROW;
     static constexpr int CHUNKS = TILE / 1024;   // 1 KiB wave loads per tile and tensor
     static constexpr int CPW = CHUNKS / NW;      // ... per wave
     static constexpr int RPC = 1024 / ROW;       // rows per 1 KiB chunk
     static constexpr int KS = D / 16;            // MFMA steps over d for S
     static constexpr int DB = D / 32;            // 32-wide blocks of d in O
+    static constexpr int KSW = UPR - 1;          // K swizzle mask (rows mod 16 or mod 8)
     static_assert(CHUNKS % NW == 0, "tile must split evenly over the waves");
-    static_assert(BM * ROW <= STAGE, "O staging must fit in one stage");
+    static_assert(RW == 32 || RW == 64, "32 or 64 query rows per wave");
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) short4 lds_short4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
-// One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes land at
-// ldst + 16*i (ldst is wave-uniform and goes to M0).  Issued as inline asm so
-// the compiler does not order later LDS reads behind it; completion is
-// awaited explicitly (vmcnt(0)) before the barrier that publishes a tile.
-// M0 is listed as clobbered; clang warns about clobbering a reserved register,
-// but no other code in these kernels keeps a value in M0 (checked in the ISA).
+// One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes come
+// from gbase + voff (voff per lane) and land at lds + 16*i (lds wave-uniform,
+// through M0).  Issued as inline asm so the compiler does not order later LDS
+// reads behind it; completion is awaited explicitly (vmcnt) before the
+// barrier that publishes a tile.  M0 is listed as clobbered; clang warns about
+// clobbering a reserved register, but no other code in these kernels keeps a
+// value in M0 (checked in the ISA).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gsrc, lds_char* ldst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)ldst);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(m0), "v"(gsrc) : "memory", "m0");
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(gbase) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -87,16 +104,24 @@ __device__ __forceinline__ i16x4 lds_tr16(const lds_char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
 }
 
+__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding)
+#define FA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdParams p) {
     using C = Bf16Cfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
     lds_char* smem = (lds_char*)smem_raw;
+    const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int n = lane & 31;     // query column owned by this lane
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;     // query column owned by this lane (in each 32-row block)
     const int g = lane >> 5;     // which half of the 32x32 block's rows
 
     // Workgroup -> (head, query tile).  Consecutive workgroup ids walk the
@@ -108,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
     int b, hq, hkv;
     head_of(p, head_x, b, hq, hkv);
     const int q0 = qt * C::BM;
-    const int qrow = q0 + w * 32 + n;
+    const int wq0 = q0 + w * C::RW;              // first row of this wave
 
     const char* Qh = reinterpret_cast<const char*>(p.q) + ((int64_t)(b * p.Hq + hq) * p.Nq) * C::ROW;
     const char* Kh = reinterpret_cast<const char*>(p.k) + ((int64_t)(b * p.Hkv + hkv) * p.Nk) * C::ROW;
@@ -119,187 +144,233 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_bf16_kernel(FwdParams p) {
     int kend = p.Nk;
     if (CAUSAL) kend = min(kend, max(q0 + C::BM + p.causal_shift, 0));
     const int n_tiles = (kend + C::BN - 1) / C::BN;
+    // Keys this wave needs (its other tiles only take part in the copies).
+    int wkend = p.Nk;
+    if (CAUSAL) wkend = min(wkend, max(wq0 + C::RW + p.causal_shift, 0));
 
     // Q rows of this lane as MFMA B operands, resident for the whole loop.
-    bf16x8 qf[C::KS];
-    if (qrow < p.Nq) {
-        const char* src = Qh + (int64_t)qrow * C::ROW;
+    bf16x8 qf[C::NQB][C::KS];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            u32x4 x = ldg16(src + (2 * ks + g) * 16);
-            x ^= p.q_sign;
-            qf[ks] = __builtin_bit_cast(bf16x8, x);
+    for (int qb = 0; qb < C::NQB; ++qb) {
+        const int qrow = wq0 + 32 * qb + n;
+        if (qrow < p.Nq) {
+            const char* src = Qh + (int64_t)qrow * C::ROW;
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                u32x4 x = ldg16(src + (2 * ks + g) * 16);
+                x ^= p.q_sign;
+                qf[qb][ks] = __builtin_bit_cast(bf16x8, x);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
         }
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
     }
 
-    // This lane's part of each 1 KiB chunk: row-in-chunk and stored unit.
+    // Loop-invariant per-lane offsets.
+    // copies: chunk c = w*CPW + t covers tile rows c*RPC .. +RPC-1
     const int c_row = lane / C::UPR;
     const int c_su = lane % C::UPR;
-
-    // Issue the global->LDS copies of key tile j into `stage`.  Rows past Nk
-    // are clamped to the last key (their scores are masked and their P is 0).
-    auto issue_tile = [&](int j, int stage) {
-        lds_char* kdst = smem + stage * C::STAGE;
-        lds_char* vdst = kdst + C::TILE;
-        const int key0 = j * C::BN;
+    uint32_t dk_off[C::CPW], dv_off[C::CPW];
 #pragma unroll
-        for (int t = 0; t < C::CPW; ++t) {
-            const int c = w * C::CPW + t;
-            const int row = c * C::RPC + c_row;
-            const int key = min(key0 + row, p.Nk - 1);
-            const int ku = c_su ^ (row & 7);                 // K: unit swizzled by row
-            const int vu = c_su ^ (2 * (row & 3));           // V: unit swizzled by 2*(row%4)
-            dma16(Kh + (int64_t)key * C::ROW + ku * 16, kdst + c * 1024);
-            dma16(Vh + (int64_t)key * C::ROW + vu * 16, vdst + c * 1024);
+    for (int t = 0; t < C::CPW; ++t) {
+        const int row = (w * C::CPW + t) * C::RPC + c_row;
+        dk_off[t] = row * C::ROW + ((c_su ^ (row & C::KSW)) << 4);
+        dv_off[t] = row * C::ROW + ((c_su ^ (2 * (row & 3))) << 4);
+    }
+    // K reads: row 32*kh + n, unit 2*ks + g, swizzled by row (kh adds 32 rows)
+    uint32_t k_off[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = n * C::ROW + (((2 * ks + g) ^ (n & C::KSW)) << 4);
+    // V^T reads: lane (n, g) sources key row 4*g + (n%16)/4 (+8, +16*st) at
+    // d = 16*(n/16) + 4*(n%4) (+32*db).  The swizzle of d-block db depends on
+    // db only through db's low bit; db >= 2 adds a constant 8 units.
+    uint32_t v_off[2];
+    {
+        const int tr_row = 4 * g + ((n & 15) >> 2);
+        const int tr_d = 16 * (n >> 4) + 4 * (n & 3);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int d = 32 * e + tr_d;
+            v_off[e] = tr_row * C::ROW + ((((d >> 3) ^ (2 * (tr_row & 3)))) << 4) + (d & 7) * 2;
+        }
+    }
+
+    // Issue the copies of key tile j into `stage`.  Full tiles use the
+    // precomputed offsets; the last, partial tile clamps rows to the last key
+    // (their scores are masked and their P is 0).
+    auto issue_tile = [&](int j, int stage) {
+        const uint32_t kdst = smem_u32 + stage * C::STAGE + w * C::CPW * 1024;
+        const uint32_t vdst = kdst + C::TILE;
+        const int key0 = j * C::BN;
+        const char* kb = Kh + (int64_t)key0 * C::ROW;
+        const char* vb = Vh + (int64_t)key0 * C::ROW;
+        if (key0 + C::BN <= p.Nk) {
+#pragma unroll
+            for (int t = 0; t < C::CPW; ++t) {
+                dma16(kb, dk_off[t], kdst + t * 1024);
+                dma16(vb, dv_off[t], vdst + t * 1024);
+            }
+        } else {
+            const int last = p.Nk - 1 - key0;
+#pragma unroll
+            for (int t = 0; t < C::CPW; ++t) {
+                const int row = (w * C::CPW + t) * C::RPC + c_row;
+                const int rc = min(row, last);
+                dma16(kb, rc * C::ROW + ((c_su ^ (row & C::KSW)) << 4), kdst + t * 1024);
+                dma16(vb, rc * C::ROW + ((c_su ^ (2 * (row & 3))) << 4), vdst + t * 1024);
+            }
         }
     };
 
-    f32x16 o[C::DB];
+    f32x16 o[C::NQB][C::DB];
+    float mref[C::NQB];      // exponent reference per row, log2 units
+    float l[C::NQB];         // this lane's part of the row sums
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
-    float mref = -INFINITY;  // exponent reference of this row, in log2 units (scaled scores)
-    float l = 0.f;           // this lane's part of the sum of exponentials (relative to mref)
+    for (int qb = 0; qb < C::NQB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) o[qb][db] = f32x16{};
+        mref[qb] = -INFINITY;
+        l[qb] = 0.f;
+    }
 
-    // Per-lane constant parts of the transposing V reads: lane (n, g) sources
-    // key row 4*g + (n%16)/4 (+8, +16*st) at d = 16*(n/16) + 4*(n%4) (+32*db).
-    const int tr_row = 4 * g + ((n & 15) >> 2);
-    const int tr_d = 16 * (n >> 4) + 4 * (n & 3);
-
-    if (n_tiles > 0) issue_tile(0, 0);
+#pragma unroll
+    for (int s0 = 0; s0 < C::NSTAGE - 1; ++s0)
+        if (s0 < n_tiles) issue_tile(s0, s0);
 
     for (int j = 0; j < n_tiles; ++j) {
-        const int stage = j & 1;
-        __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0): this wave's copies of tile j landed
-        __syncthreads();                                 // ... and every other wave's
-        if (j + 1 < n_tiles) issue_tile(j + 1, stage ^ 1);
+        const int stage = j % C::NSTAGE;
+        // wait for this wave's copies of tile j (later tiles may stay in flight)
+        if (C::NSTAGE == 2 || j + 1 >= n_tiles) {
+            FA_WAIT_VMCNT(0);
+        } else {
+            FA_WAIT_VMCNT(2 * C::CPW);
+        }
+        __syncthreads();
+        if (j + C::NSTAGE - 1 < n_tiles) issue_tile(j + C::NSTAGE - 1, (j + C::NSTAGE - 1) % C::NSTAGE);
+
+        const int key0 = j * C::BN;
+        if (key0 >= wkend) continue;            // every key of this tile is hidden from this wave
         const lds_char* kb = smem + stage * C::STAGE;
         const lds_char* vb = kb + C::TILE;
 
-        // S^T for 2 x 32 keys against this wave's 32 queries
-        f32x16 s[2];
+        const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > wq0 + p.causal_shift);
+
+        // Two 32-key halves, each: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+        // The reference decision is made per half, so the halves are independent
+        // steps of the same recurrence.
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            s[h] = f32x16{};
-            const int row = 32 * h + n;
+        for (int kh = 0; kh < 2; ++kh) {
+            f32x16 s[C::NQB];
+#pragma unroll
+            for (int qb = 0; qb < C::NQB; ++qb) s[qb] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const int cu = 2 * ks + g;
-                const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-                    kb + row * C::ROW + ((cu ^ (row & 7)) << 4));
-                s[h] = mfma_bf16_32x32x16(a, qf[ks], s[h]);
-            }
-        }
-
-        // Mask: keys past Nk and, for causal problems, keys after the
-        // query's diagonal.  Only tiles that straddle either edge pay for it.
-        const int key0 = j * C::BN;
-        const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > q0 + p.causal_shift);
-        const int lim = CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1;
-        if (need_mask) {
+                const bf16x8 a = lds_b128(kb + k_off[ks] + kh * 32 * C::ROW);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+                for (int qb = 0; qb < C::NQB; ++qb) s[qb] = mfma_bf16_32x32x16(a, qf[qb][ks], s[qb]);
+            }
+
+            // Mask keys past Nk and, for causal problems, keys after each
+            // query's diagonal.  Only tiles that straddle either edge pay.
+            if (need_mask) {
+#pragma unroll
+                for (int qb = 0; qb < C::NQB; ++qb) {
+                    const int qrow = wq0 + 32 * qb + n;
+                    const int lim = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - key0 - 32 * kh - 4 * g;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (8 * (i >> 2) + (i & 3) > lim) s[qb][i] = -INFINITY;
+                }
+            }
+
+            bf16x8 pb[C::NQB][2];
+#pragma unroll
+            for (int qb = 0; qb < C::NQB; ++qb) {
+                float mx = s[qb][0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[qb][i]);
+                mx = pair_max(mx) * p.c;                         // half-tile max, log2 units
+                const bool move = mx > mref[qb] + kRescaleLog2;  // false while nothing is visible
+                if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                    const float mnew = move ? mx : mref[qb];
+                    const float alpha = move ? ((mref[qb] == -INFINITY) ? 0.f : fast_exp2(mref[qb] - mnew)) : 1.f;
+                    mref[qb] = mnew;
+                    l[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) o[qb][db] *= alpha;
+                }
+                const float mb = (mref[qb] == -INFINITY) ? 0.f : mref[qb];
+                float rs = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = key0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (key > lim) s[h][i] = -INFINITY;
+                    const float e = fast_exp2(fmaf(s[qb][i], p.c, -mb));
+                    s[qb][i] = e;
+                    rs += e;
                 }
-        }
-
-        // Online softmax with a lazily moved reference.
-        float mx = -INFINITY;
+                l[qb] += rs;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+                for (int h8 = 0; h8 < 2; ++h8) {
+                    u32x4 pk;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
-        mx = pair_max(mx) * p.c;                         // tile max in log2 units (-inf if none visible)
-        const bool move = mx > mref + kRescaleLog2;      // false while nothing is visible
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {    // some row of this wave moves its reference
-            const float mnew = move ? mx : mref;
-            const float alpha = move ? ((mref == -INFINITY) ? 0.f : fast_exp2(mref - mnew)) : 1.f;
-            mref = mnew;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
-        }
-        const float mb = (mref == -INFINITY) ? 0.f : mref;
-
-        float rs = 0.f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float e = fast_exp2(fmaf(s[h][i], p.c, -mb));
-                if (need_mask) {
-                    const int key = key0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (key > lim) e = 0.f;
+                    for (int e2 = 0; e2 < 4; ++e2)
+                        pk[e2] = pack_bf16x2(s[qb][8 * h8 + 2 * e2], s[qb][8 * h8 + 2 * e2 + 1]);
+                    pb[qb][h8] = __builtin_bit_cast(bf16x8, pk);
                 }
-                s[h][i] = e;
-                rs += e;
             }
-        l += rs;
-
-        // O^T += V^T P^T over 4 steps of 16 keys
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int h = st >> 1, i0 = 8 * (st & 1);
-            u32x4 pk;
-            pk[0] = pack_bf16x2(s[h][i0 + 0], s[h][i0 + 1]);
-            pk[1] = pack_bf16x2(s[h][i0 + 2], s[h][i0 + 3]);
-            pk[2] = pack_bf16x2(s[h][i0 + 4], s[h][i0 + 5]);
-            pk[3] = pack_bf16x2(s[h][i0 + 6], s[h][i0 + 7]);
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
-            const int r0 = 16 * st + tr_row;               // key rows r0 (slots 0-3) and r0 + 8 (slots 4-7)
+            for (int h8 = 0; h8 < 2; ++h8) {
+                const int st = 2 * kh + h8;                      // 16-key step within the tile
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                const int d = 32 * db + tr_d;
-                const int u = d >> 3, half = (d & 7) * 2;
-                const i16x4 lo = lds_tr16(vb + r0 * C::ROW + ((u ^ (2 * (r0 & 3))) << 4) + half);
-                const i16x4 hi = lds_tr16(vb + (r0 + 8) * C::ROW + ((u ^ (2 * ((r0 + 8) & 3))) << 4) + half);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[db] = mfma_bf16_32x32x16(a, pb, o[db]);
+                for (int db = 0; db < C::DB; ++db) {
+                    const lds_char* vp = vb + v_off[db & 1] + (db >> 1) * 128 + 16 * st * C::ROW;
+                    const i16x4 lo = lds_tr16(vp);
+                    const i16x4 hi = lds_tr16(vp + 8 * C::ROW);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int qb = 0; qb < C::NQB; ++qb) o[qb][db] = mfma_bf16_32x32x16(a, pb[qb][h8], o[qb][db]);
+                }
             }
         }
     }
 
-    // Epilogue: normalise once, stage O as bf16 in LDS (the stage no longer
-    // read), then write whole rows with 16-byte coalesced stores.
-    const float lt = pair_sum(l);
-    const float inv = lt > 0.f ? p.o_scale / lt : 0.f;
+    // Epilogue: normalise once, stage O as bf16 in LDS, then write whole rows
+    // with 16-byte coalesced stores.
     __syncthreads();
-    lds_char* ost = smem + (n_tiles & 1) * C::STAGE;
-    {
-        const int row = w * 32 + n;
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+        const float lt = pair_sum(l[qb]);
+        const float inv = lt > 0.f ? p.o_scale / lt : 0.f;
+        const int row = w * C::RW + 32 * qb + n;          // row within the workgroup tile
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const int u = 4 * db + i4;               // 16-byte unit of d = 32*db + 8*i4 + 4*g
+                const int u = 4 * db + i4;                // 16-byte unit of d = 32*db + 8*i4 + 4*g
                 u32x2 val;
-                val[0] = pack_bf16x2(o[db][4 * i4 + 0] * inv, o[db][4 * i4 + 1] * inv);
-                val[1] = pack_bf16x2(o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv);
+                val[0] = pack_bf16x2(o[qb][db][4 * i4 + 0] * inv, o[qb][db][4 * i4 + 1] * inv);
+                val[1] = pack_bf16x2(o[qb][db][4 * i4 + 2] * inv, o[qb][db][4 * i4 + 3] * inv);
                 *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-                    ost + row * C::ROW + ((u ^ (row & 7)) << 4) + 8 * g) = val;
+                    smem + row * C::ROW + ((u ^ (row & C::KSW)) << 4) + 8 * g) = val;
             }
-    }
-    if (p.lse != nullptr && g == 0 && qrow < p.Nq) {
-        const float v = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-        p.lse[(int64_t)(b * p.Hq + hq) * p.Nq + qrow] = v;
+        const int qrow = wq0 + 32 * qb + n;
+        if (p.lse != nullptr && g == 0 && qrow < p.Nq) {
+            const float v = lt > 0.f ? (mref[qb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+            p.lse[(int64_t)(b * p.Hq + hq) * p.Nq + qrow] = v;
+        }
     }
     __syncthreads();
     char* Oh = reinterpret_cast<char*>(p.o) + ((int64_t)(b * p.Hq + hq) * p.Nq) * C::ROW;
 #pragma unroll
-    for (int it = 0; it < 32 * C::UPR / 64; ++it) {
+    for (int it = 0; it < C::RW * C::UPR / 64; ++it) {
         const int f = it * 64 + lane;
-        const int row = w * 32 + f / C::UPR;
+        const int row = w * C::RW + f / C::UPR;
         const int su = f % C::UPR;
         const int grow = q0 + row;
         if (grow < p.Nq) {
             const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                ost + row * C::ROW + su * 16);
-            *reinterpret_cast<u32x4*>(Oh + (int64_t)grow * C::ROW + ((su ^ (row & 7)) << 4)) = v;
+                smem + row * C::ROW + su * 16);
+            *reinterpret_cast<u32x4*>(Oh + (int64_t)grow * C::ROW + ((su ^ (row & C::KSW)) << 4)) = v;
         }
     }
 }
