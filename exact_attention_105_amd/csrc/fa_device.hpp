@@ -22,6 +22,7 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -38,7 +39,7 @@ struct FwdParams {
     int n_heads;        // B * Hq
     int causal_shift;   // Nk - Nq: key j visible to query i iff j <= i + causal_shift
     float c;            // |scale| (* sq * sk for fp8) * log2(e): exponent of 2 per raw score
-    float o_scale;      // multiplies the normalised output (sv * 2^-8 for fp8, 1 for bf16)
+    float o_scale;      // multiplies the normalised output (sv for fp8, 1 for bf16)
     uint32_t q_sign;    // XOR mask applied to Q bit patterns (flips the sign when scale < 0)
 };
 
@@ -94,6 +95,49 @@ __device__ __forceinline__ void head_of(const FwdParams& p, int x, int& b, int& 
     b = kvflat / p.Hkv;
     hkv = kvflat % p.Hkv;
     hq = hkv * p.group + gi;
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+// One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes come
+// from gbase + voff (voff per lane) and land at lds + 16*i (lds wave-uniform,
+// through M0).  Issued as inline asm so the compiler does not order later LDS
+// reads behind it; completion is awaited explicitly (vmcnt) before the
+// barrier that publishes a tile.  M0 is listed as clobbered; clang warns about
+// clobbering a reserved register, but no other code in these kernels keeps a
+// value in M0 (checked in the ISA).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds), "v"(voff), "s"(gbase) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ i16x4 lds_tr16(const lds_char* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
+}
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding)
+#define FA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
+
+// 8 bytes per lane through the 8-bit transposing LDS read: within each group
+// of 16 lanes, lane i receives byte i%8 of the 8 bytes read by lanes
+// i/8 + 2r, r = 0..7 (in that order).
+__device__ __forceinline__ u32x2 lds_tr8(const lds_char* p) {
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+    return u32x2{(uint32_t)r[0], (uint32_t)r[1]};
+}
+
+__device__ __forceinline__ u32x4 lds_u128(const lds_char* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p);
 }
 
 }  // namespace fa

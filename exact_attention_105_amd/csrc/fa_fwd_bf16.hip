@@ -81,36 +81,6 @@ struct Bf16Cfg {
     static_assert(RW == 32 || RW == 64, "32 or 64 query rows per wave");
 };
 
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-
-// One wave-wide 16-byte-per-lane copy global -> LDS: lane i's 16 bytes come
-// from gbase + voff (voff per lane) and land at lds + 16*i (lds wave-uniform,
-// through M0).  Issued as inline asm so the compiler does not order later LDS
-// reads behind it; completion is awaited explicitly (vmcnt) before the
-// barrier that publishes a tile.  M0 is listed as clobbered; clang warns about
-// clobbering a reserved register, but no other code in these kernels keeps a
-// value in M0 (checked in the ISA).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds), "v"(voff), "s"(gbase) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ i16x4 lds_tr16(const lds_char* p) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-}
-
-__device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
-}
-
-// vmcnt(n) with the other counters left alone (gfx9 encoding)
-#define FA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdParams p) {
     using C = Bf16Cfg<D>;

@@ -3,40 +3,58 @@
 // Low-precision attention (page "FlashAttention-3 (DE)", systems-analysis.ru,
 // section on low precision: FP8 doubles the matrix throughput at the cost of
 // dynamic range).  The structure follows the bf16 kernel (fa_fwd_bf16.hip):
-// 128 query rows per workgroup, 64-key K/V tiles in double-buffered LDS, the
-// query index on the MFMA column side so each lane owns one query row, and
-// the online softmax in registers.  Differences:
-//   * both products use v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3 -> fp32);
+// BM = 128 query rows per workgroup (32 per wave, two workgroups per CU),
+// 64-key K/V tiles copied straight into double-buffered LDS, the query index
+// on the MFMA column side so each lane owns one query row, and the online
+// softmax with a lazily moved reference in registers.  Differences:
+//   * both products use v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3 -> fp32); one
+//     S^T product covers 64 d and one O^T product covers the whole 64-key tile;
 //   * the per-tensor scales are folded in: the exponent constant is
-//     |scale| * sq * sk * log2(e), and the normalised output is multiplied
-//     by sv;
-//   * P is quantised to e4m3 for the second product after multiplying by
-//     2^8 (added to the exp2 argument), so probabilities down to 2^-14 stay
-//     in e4m3's normal range; the row sum uses the unquantised fp32 values
-//     in the same 2^8 units, and the log-sum-exp removes the offset again.
-// One 32x32x64 product covers a 64-key tile, so each lane feeds 32 keys of P:
-// the 16 scores it holds of each 32-key half, in register order.  V^T rows
-// in LDS hold those keys at positions 32*(l/32) + slot, which maps 4-key
-// units as pu = 8*(ku & 1) + 4*(ku >> 3) + ((ku >> 1) & 3).
+//     |scale| * sq * sk * log2(e), and the normalised output is multiplied by sv;
+//   * P is quantised to e4m3 for the second product.  The exponentials carry
+//     a 2^kP8Offset factor and the reference moves as soon as the running max
+//     exceeds it by more than 2^kP8Slack, so P stays below 2^(offset+slack) =
+//     256 < 448 (e4m3's largest value) and probabilities down to ~2^-12 of the
+//     reference stay in e4m3's normal range.  The row sums use the
+//     unquantised fp32 values in the same units; the log-sum-exp removes the
+//     offset again;
+//   * V^T comes from row-major V through the 8-bit transposing LDS read
+//     ds_read_b64_tr_b8 (16 lanes read 8 key rows x 16 bytes; each lane
+//     receives one d column of 8 keys); four reads give a lane the 32 keys of
+//     its P operand, in the order the scores sit in its registers.
+// LDS swizzles (16-byte units, 128-byte rows): K by (row/2) mod 8, so the 16
+// rows one ds_read_b128 touches hit distinct banks; V by
+// 2*((row/2 mod 2) + 2*(row/8 mod 2)), which separates the 8 rows one
+// transposing read touches.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
+
+constexpr float kP8Offset = 6.0f;   // log2 of the factor carried by the exponentials
+constexpr float kP8Slack = 2.0f;    // log2 growth of the max tolerated before rescaling
 
 struct Fp8Cfg {
     static constexpr int D = 128;
     static constexpr int NW = 4;
     static constexpr int BM = 32 * NW;
     static constexpr int BN = 64;
-    static constexpr int KROW = D;              // bytes of one K row
-    static constexpr int VROW = BN;             // bytes of one V^T row
-    static constexpr int K_BYTES = BN * D;
-    static constexpr int V_BYTES = BN * D;
-    static constexpr int STAGE = K_BYTES + V_BYTES;
-    static constexpr int LDS = 2 * STAGE;
-    static constexpr int CU = D / 16;           // 16-byte units per K row
-    static constexpr int K_UNITS = BN * CU / 256;
+    static constexpr int ROW = D;               // bytes of one K or V row
+    static constexpr int UPR = D / 16;          // 16-byte units per row (8)
+    static constexpr int TILE = BN * ROW;       // 8 KiB
+    static constexpr int STAGE = 2 * TILE;
+    static constexpr int NSTAGE = 2;
+    static constexpr int OROW = D * 2;          // bytes of one bf16 O row
+    static constexpr int LDS = NSTAGE * STAGE > BM * OROW ? NSTAGE * STAGE : BM * OROW;
+    static constexpr int CHUNKS = TILE / 1024;  // 8
+    static constexpr int CPW = CHUNKS / NW;     // 2
+    static constexpr int RPC = 1024 / ROW;      // 8 rows per chunk
+    static constexpr int DB = D / 32;           // 32-wide blocks of d in O
+    static_assert(CHUNKS % NW == 0, "tile must split evenly over the waves");
 };
+
+__device__ __forceinline__ int k8_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int v8_swz(int row) { return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1)); }
 
 // Four fp32 values to four e4m3 bytes (round to nearest even, OCP e4m3 on gfx950).
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
@@ -46,14 +64,16 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_fwd_fp8_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
     using C = Fp8Cfg;
     constexpr int D = C::D;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+    lds_char* smem = (lds_char*)smem_raw;
+    const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31;
     const int g = lane >> 5;
 
@@ -63,7 +83,8 @@ __global__ __launch_bounds__(256) void fa_fwd_fp8_kernel(FwdParams p) {
     int b, hq, hkv;
     head_of(p, head_x, b, hq, hkv);
     const int q0 = qt * C::BM;
-    const int qrow = q0 + w * 32 + n;
+    const int wq0 = q0 + w * 32;
+    const int qrow = wq0 + n;
 
     const char* Qh = reinterpret_cast<const char*>(p.q) + ((int64_t)(b * p.Hq + hq) * p.Nq) * D;
     const char* Kh = reinterpret_cast<const char*>(p.k) + ((int64_t)(b * p.Hkv + hkv) * p.Nk) * D;
@@ -72,6 +93,8 @@ __global__ __launch_bounds__(256) void fa_fwd_fp8_kernel(FwdParams p) {
     int kend = p.Nk;
     if (CAUSAL) kend = min(kend, max(q0 + C::BM + p.causal_shift, 0));
     const int n_tiles = (kend + C::BN - 1) / C::BN;
+    int wkend = p.Nk;
+    if (CAUSAL) wkend = min(wkend, max(wq0 + 32 + p.causal_shift, 0));
 
     // Q as B operands: k-step ks covers d = 64*ks + 32*g + [0, 32).
     i32x8 qf[2];
@@ -91,176 +114,182 @@ __global__ __launch_bounds__(256) void fa_fwd_fp8_kernel(FwdParams p) {
         qf[1] = i32x8{};
     }
 
-    u32x4 kreg[C::K_UNITS];
-    u32x2 vreg[4];
-    const int vku = tid & 15;     // 4-key unit of the V block this thread moves
-    const int vc = tid >> 4;      // 8-wide d chunk
+    // Loop-invariant per-lane offsets.
+    const int c_row = lane / C::UPR;
+    const int c_su = lane % C::UPR;
+    uint32_t dk_off[C::CPW], dv_off[C::CPW];
+#pragma unroll
+    for (int t = 0; t < C::CPW; ++t) {
+        const int row = (w * C::CPW + t) * C::RPC + c_row;
+        dk_off[t] = row * C::ROW + ((c_su ^ k8_swz(row)) << 4);
+        dv_off[t] = row * C::ROW + ((c_su ^ v8_swz(row)) << 4);
+    }
+    // K reads: row 32*kh + n, units 4*ks + 2*g + e (e = 0, 1); kh adds 32 rows.
+    uint32_t k_off[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) k_off[ks][e] = n * C::ROW + (((4 * ks + 2 * g + e) ^ k8_swz(n)) << 4);
+    // V^T reads: read q (0..3) gives P slots 8q..8q+7 = keys 16q + 8*(r/4) + 4g + r%4,
+    // r = 0..7; this lane sources r = (n%16)/2 at d = 32*db + 16*(n/16) + 8*(n%2).
+    uint32_t v_off[C::DB];
+    {
+        const int r = (n & 15) >> 1;
+        const int vrow = 8 * (r >> 2) + 4 * g + (r & 3);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const int unit = 2 * db + (n >> 4);
+            v_off[db] = vrow * C::ROW + ((unit ^ v8_swz(vrow)) << 4) + 8 * (n & 1);
+        }
+    }
 
-    auto load_tile = [&](int j) {
+    auto issue_tile = [&](int j, int stage) {
+        const uint32_t kdst = smem_u32 + stage * C::STAGE + w * C::CPW * 1024;
+        const uint32_t vdst = kdst + C::TILE;
         const int key0 = j * C::BN;
+        const char* kb = Kh + (int64_t)key0 * C::ROW;
+        const char* vb = Vh + (int64_t)key0 * C::ROW;
+        if (key0 + C::BN <= p.Nk) {
 #pragma unroll
-        for (int r = 0; r < C::K_UNITS; ++r) {
-            const int u = tid + 256 * r;
-            const int row = u / C::CU, cu = u % C::CU;
-            const int key = key0 + row;
-            kreg[r] = key < p.Nk ? ldg16(Kh + (int64_t)key * D + cu * 16) : u32x4{0, 0, 0, 0};
-        }
+            for (int t = 0; t < C::CPW; ++t) {
+                dma16(kb, dk_off[t], kdst + t * 1024);
+                dma16(vb, dv_off[t], vdst + t * 1024);
+            }
+        } else {
+            const int last = p.Nk - 1 - key0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = key0 + 4 * vku + r;
-            vreg[r] = key < p.Nk ? *reinterpret_cast<const u32x2*>(Vh + (int64_t)key * D + vc * 8)
-                                 : u32x2{0, 0};
-        }
-    };
-
-    auto store_tile = [&](int stage) {
-        char* kb = smem + stage * C::STAGE;
-        char* vb = kb + C::K_BYTES;
-#pragma unroll
-        for (int r = 0; r < C::K_UNITS; ++r) {
-            const int u = tid + 256 * r;
-            const int row = u / C::CU, cu = u % C::CU;
-            lds_store16(kb, row * C::KROW + ((cu ^ (row & 7)) << 4), kreg[r]);
-        }
-        // 4 keys x 8 bytes -> 8 rows of V^T x 4 keys (byte transpose with v_perm)
-        const int pu = 8 * (vku & 1) + 4 * (vku >> 3) + ((vku >> 1) & 3);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint32_t A = vreg[0][half], Bv = vreg[1][half], Cv = vreg[2][half], Dv = vreg[3][half];
-            const uint32_t ab_lo = __builtin_amdgcn_perm(Bv, A, 0x05010400u);
-            const uint32_t ab_hi = __builtin_amdgcn_perm(Bv, A, 0x07030602u);
-            const uint32_t cd_lo = __builtin_amdgcn_perm(Dv, Cv, 0x05010400u);
-            const uint32_t cd_hi = __builtin_amdgcn_perm(Dv, Cv, 0x07030602u);
-            const uint32_t out[4] = {__builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u),
-                                     __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u),
-                                     __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u),
-                                     __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u)};
-#pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) {
-                const int d = vc * 8 + half * 4 + t4;
-                const int unit = (pu >> 2) ^ ((d >> 1) & 3);
-                *reinterpret_cast<uint32_t*>(vb + d * C::VROW + (unit << 4) + ((pu & 3) << 2)) = out[t4];
+            for (int t = 0; t < C::CPW; ++t) {
+                const int row = (w * C::CPW + t) * C::RPC + c_row;
+                const int rc = min(row, last);
+                dma16(kb, rc * C::ROW + ((c_su ^ k8_swz(row)) << 4), kdst + t * 1024);
+                dma16(vb, rc * C::ROW + ((c_su ^ v8_swz(row)) << 4), vdst + t * 1024);
             }
         }
     };
 
-    f32x16 o[4];
+    f32x16 o[C::DB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-    float m = -INFINITY;
-    float l = 0.f;
+    for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
+    float mref = -INFINITY;   // exponent reference of this row, log2 units
+    float l = 0.f;            // this lane's part of the row sum, times 2^kP8Offset
 
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
+    if (n_tiles > 0) issue_tile(0, 0);
 
     for (int j = 0; j < n_tiles; ++j) {
         const int stage = j & 1;
-        if (j + 1 < n_tiles) load_tile(j + 1);
-        const char* kb = smem + stage * C::STAGE;
-        const char* vb = kb + C::K_BYTES;
+        FA_WAIT_VMCNT(0);
+        __syncthreads();
+        if (j + 1 < n_tiles) issue_tile(j + 1, stage ^ 1);
+
+        const int key0 = j * C::BN;
+        if (key0 >= wkend) continue;
+        const lds_char* kb = smem + stage * C::STAGE;
+        const lds_char* vb = kb + C::TILE;
 
         f32x16 s[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            s[h] = f32x16{};
-            const int row = 32 * h + n;
+        for (int kh = 0; kh < 2; ++kh) {
+            s[kh] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int u0 = 4 * ks + 2 * g;
-                const u32x4 lo = lds_load16(kb, row * C::KROW + ((u0 ^ (row & 7)) << 4));
-                const u32x4 hi = lds_load16(kb, row * C::KROW + (((u0 + 1) ^ (row & 7)) << 4));
+                const u32x4 lo = lds_u128(kb + k_off[ks][0] + kh * 32 * C::ROW);
+                const u32x4 hi = lds_u128(kb + k_off[ks][1] + kh * 32 * C::ROW);
                 const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                s[h] = mfma_fp8_32x32x64(a, qf[ks], s[h]);
+                s[kh] = mfma_fp8_32x32x64(a, qf[ks], s[kh]);
             }
         }
 
-        const int key0 = j * C::BN;
-        const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > q0 + p.causal_shift);
-        const int lim = CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1;
+        const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > wq0 + p.causal_shift);
         if (need_mask) {
+            const int lim = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - key0 - 4 * g;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = key0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (key > lim) s[h][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kh + 8 * (i >> 2) + (i & 3) > lim) s[kh][i] = -INFINITY;
         }
 
-        float mx = -INFINITY;
+        float mx = s[0][0];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m, mx);
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float mc = m_ref * p.c;
-        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m * p.c - mc);
-        m = m_new;
-
-        // probabilities times 2^8
-        const float off = 8.f - mc;
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kh][i]);
+        mx = pair_max(mx) * p.c;
+        const bool move = mx > mref + kP8Slack;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+            const float mnew = move ? mx : mref;
+            const float alpha = move ? ((mref == -INFINITY) ? 0.f : fast_exp2(mref - mnew)) : 1.f;
+            mref = mnew;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+        }
+        const float off = kP8Offset - ((mref == -INFINITY) ? 0.f : mref);
         float rs = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float e = fast_exp2(fmaf(s[h][i], p.c, off));
-                if (need_mask) {
-                    const int key = key0 + 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
-                    if (key > lim) e = 0.f;
-                }
-                s[h][i] = e;
+                const float e = fast_exp2(fmaf(s[kh][i], p.c, off));
+                s[kh][i] = e;
                 rs += e;
             }
-        l = l * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        l += rs;
 
         i32x8 pb;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)
-                pb[4 * h + q4] = (int)pack_fp8x4(s[h][4 * q4], s[h][4 * q4 + 1], s[h][4 * q4 + 2], s[h][4 * q4 + 3]);
+                pb[4 * kh + q4] = (int)pack_fp8x4(s[kh][4 * q4], s[kh][4 * q4 + 1], s[kh][4 * q4 + 2], s[kh][4 * q4 + 3]);
 
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int d = 32 * db + n;
-            const int sw = (d >> 1) & 3;
-            const u32x4 lo = lds_load16(vb, d * C::VROW + (((2 * g) ^ sw) << 4));
-            const u32x4 hi = lds_load16(vb, d * C::VROW + (((2 * g + 1) ^ sw) << 4));
-            const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        for (int db = 0; db < C::DB; ++db) {
+            i32x8 a;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x2 t = lds_tr8(vb + v_off[db] + 16 * q * C::ROW);
+                a[2 * q] = (int)t[0];
+                a[2 * q + 1] = (int)t[1];
+            }
             o[db] = mfma_fp8_32x32x64(a, pb, o[db]);
         }
-
-        if (j + 1 < n_tiles) store_tile(stage ^ 1);
-        __syncthreads();
     }
 
+    // Epilogue: normalise, stage O as bf16 in LDS, coalesced 16-byte stores.
     const float lt = pair_sum(l);
-    if (qrow < p.Nq) {
-        const float inv = lt > 0.f ? p.o_scale / lt : 0.f;
-        char* Orow = reinterpret_cast<char*>(p.o) + (((int64_t)(b * p.Hq + hq) * p.Nq + qrow) * D) * 2;
+    const float inv = lt > 0.f ? p.o_scale / lt : 0.f;
+    __syncthreads();
+    {
+        const int row = w * 32 + n;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const int d = 32 * db + 8 * i4 + 4 * g;
+                const int u = 4 * db + i4;
                 u32x2 val;
                 val[0] = pack_bf16x2(o[db][4 * i4 + 0] * inv, o[db][4 * i4 + 1] * inv);
                 val[1] = pack_bf16x2(o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(Orow + d * 2) = val;
+                *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                    smem + row * C::OROW + ((u ^ (row & 15)) << 4) + 8 * g) = val;
             }
-        if (p.lse != nullptr && g == 0) {
-            const float v = lt > 0.f ? (m * p.c + __builtin_amdgcn_logf(lt) - 8.f) * kLn2 : -INFINITY;
-            p.lse[(int64_t)(b * p.Hq + hq) * p.Nq + qrow] = v;
+    }
+    if (p.lse != nullptr && g == 0 && qrow < p.Nq) {
+        const float v = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt) - kP8Offset) * kLn2 : -INFINITY;
+        p.lse[(int64_t)(b * p.Hq + hq) * p.Nq + qrow] = v;
+    }
+    __syncthreads();
+    char* Oh = reinterpret_cast<char*>(p.o) + ((int64_t)(b * p.Hq + hq) * p.Nq) * C::OROW;
+#pragma unroll
+    for (int it = 0; it < 32 * 16 / 64; ++it) {
+        const int f = it * 64 + lane;
+        const int row = w * 32 + f / 16;
+        const int su = f % 16;
+        const int grow = q0 + row;
+        if (grow < p.Nq) {
+            const u32x4 v = lds_u128(smem + row * C::OROW + su * 16);
+            *reinterpret_cast<u32x4*>(Oh + (int64_t)grow * C::OROW + ((su ^ (row & 15)) << 4)) = v;
         }
     }
 }
