@@ -91,8 +91,12 @@ extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void*
     // exponent reference, so the weights stay exactly uniform.
     p.c = fmaxf(p.c, FLT_MIN);
 
-    hipError_t err = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(p, d, causal != 0, stream)
-                                              : fa::launch_fwd_fp8(p, d, causal != 0, stream);
+    hipError_t err;
+    if (dtype == FA_DTYPE_BF16)
+        err = fa::decode_applies(p, d, true) ? fa::launch_fwd_decode(p, causal != 0, stream)
+                                             : fa::launch_fwd_bf16(p, d, causal != 0, stream);
+    else
+        err = fa::launch_fwd_fp8(p, d, causal != 0, stream);
     return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
 }
 

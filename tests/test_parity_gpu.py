@@ -205,3 +205,34 @@ def test_config_fp8():
     o_ref, lse_ref = oracle_ref(x, "e4m3", cfg.causal, cfg.scale, rows=rows)
     compare_fp8(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
                 f"fp8 ({rows.size} sampled rows)")
+
+
+# ------------------------------------------------------------------ few query rows (decode path)
+# bf16, d = 128, Nq <= 16 runs the grouped-query packed decode kernel:
+# packed rows Nq*G up to and beyond one 32-row tile, key counts that are not
+# multiples of the 32-key tile or smaller than the four per-wave key ranges.
+DECODE = [
+    (2, 32, 8, 1, 8192, True),
+    (3, 8, 2, 1, 1000, False),
+    (2, 4, 4, 1, 1, True),
+    (1, 4, 1, 1, 31, False),
+    (1, 8, 1, 2, 33, True),
+    (2, 16, 2, 5, 100, True),
+    (1, 16, 4, 16, 300, True),
+    (1, 16, 4, 16, 300, False),
+    (1, 8, 8, 3, 129, True),
+    (1, 2, 2, 16, 16, True),
+    (1, 2, 1, 7, 4, True),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}Nq{s[3]}Nk{s[4]}{'c' if s[5] else 'n'}"
+                                               for s in DECODE])
+def test_decode_bf16(shape):
+    B, Hq, Hkv, Nq, Nk, causal = shape
+    say(f"decode case {shape}")
+    x = make_inputs(B, Hq, Hkv, Nq, Nk, 128, "bf16", 3000 + sum(shape))
+    scale = 1.0 / math.sqrt(128)
+    o, lse = run_gpu(x, "bf16", causal, scale)
+    o_ref, lse_ref = oracle_ref(x, "bf16", causal, scale)
+    compare_bf16(o, lse, o_ref, lse_ref, f"decode {shape}")
