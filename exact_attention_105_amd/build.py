@@ -34,11 +34,12 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, jobs: int = 4, extra_flags=(), out: str = LIB,
-          objdir: str | None = None) -> str:
+          objdir: str | None = None, csrc: str = CSRC) -> str:
     """Compile every source for gfx950 and link the library (libfa.so by default).
 
     ``extra_flags`` are appended to every hipcc compile (e.g. -D tuning macros);
-    ``out``/``objdir`` place a variant build elsewhere.  Returns the library path.
+    ``out``/``objdir``/``csrc`` build a variant from another source tree into
+    another place.  Returns the library path.
     """
     objdir = objdir or os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -47,8 +48,8 @@ def build(verbose: bool = False, jobs: int = 4, extra_flags=(), out: str = LIB,
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c",
-               os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", csrc, "-c",
+               os.path.join(csrc, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,

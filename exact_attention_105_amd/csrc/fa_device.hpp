@@ -66,6 +66,26 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum and sum of the 16 accumulator values of one lane, as shallow trees
+// (max3 steps / pairwise adds) instead of 15-long dependency chains.
+__device__ __forceinline__ float max16(const f32x16& s) {
+    const float a = fmaxf(fmaxf(s[0], s[1]), s[2]);
+    const float b = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    const float c = fmaxf(fmaxf(s[6], s[7]), s[8]);
+    const float d = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    const float e = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), s[15]));
+}
+
+__device__ __forceinline__ float sum16(const f32x16& s) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = s[2 * i] + s[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+    return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
 // Two fp32 values to packed bf16 (round to nearest even, v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2 v = {lo, hi};
@@ -111,8 +131,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);   // keeps the operand scalar
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds), "v"(voff), "s"(gbase) : "memory", "m0");
+                 :: "s"(m0), "v"(voff), "s"(gbase) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

@@ -40,6 +40,8 @@
 // with far fewer rescales (the idea of page "FlashAttention 4", centron.de,
 // section on smarter online-softmax rescaling; the threshold is this
 // library's choice).  A wave skips the O rescale when none of its rows moved.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -53,9 +55,6 @@ constexpr float kRescaleLog2 = 8.0f;
 #ifndef FA_BF16_RW64
 #define FA_BF16_RW64 32      // query rows per wave at d = 64 (32 or 64)
 #endif
-#ifndef FA_BF16_NSTAGE
-#define FA_BF16_NSTAGE 2     // K/V tiles resident in LDS (2 or 3)
-#endif
 
 template <int D>
 struct Bf16Cfg {
@@ -64,7 +63,7 @@ struct Bf16Cfg {
     static constexpr int NQB = RW / 32;          // 32-row query blocks per wave
     static constexpr int BM = RW * NW;           // query rows per workgroup
     static constexpr int BN = 64;                // keys per K/V tile
-    static constexpr int NSTAGE = FA_BF16_NSTAGE;
+    static constexpr int NSTAGE = 2;             // K/V tiles resident in LDS
     static constexpr int OCC = RW == 32 ? 2 : 1; // workgroups per CU the registers allow
     static constexpr int ROW = D * 2;            // bytes of one K or V row in LDS
     static constexpr int UPR = D / 8;            // 16-byte units per row
@@ -204,43 +203,41 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         l[qb] = 0.f;
     }
 
-#pragma unroll
-    for (int s0 = 0; s0 < C::NSTAGE - 1; ++s0)
-        if (s0 < n_tiles) issue_tile(s0, s0);
-
-    for (int j = 0; j < n_tiles; ++j) {
-        const int stage = j % C::NSTAGE;
-        // wait for this wave's copies of tile j (later tiles may stay in flight)
-        if (C::NSTAGE == 2 || j + 1 >= n_tiles) {
-            FA_WAIT_VMCNT(0);
-        } else {
-            FA_WAIT_VMCNT(2 * C::CPW);
-        }
-        __syncthreads();
-        if (j + C::NSTAGE - 1 < n_tiles) issue_tile(j + C::NSTAGE - 1, (j + C::NSTAGE - 1) % C::NSTAGE);
+    // One key tile: wait for its copies, start the next tile's copies, then
+    // compute.  Templated on the LDS stage so every LDS address below is a
+    // loop-invariant per-lane register plus an immediate offset.
+    auto tile = [&](auto stage_c, int j) {
+        constexpr int STG = decltype(stage_c)::value;
+        FA_WAIT_VMCNT(0);                       // this wave's copies of tile j landed
+        __syncthreads();                        // ... and every other wave's
+        if (j + 1 < n_tiles) issue_tile(j + 1, STG ^ 1);
 
         const int key0 = j * C::BN;
-        if (key0 >= wkend) continue;            // every key of this tile is hidden from this wave
-        const lds_char* kb = smem + stage * C::STAGE;
+        if (key0 >= wkend) return;              // every key of this tile is hidden from this wave
+        const lds_char* kb = smem + STG * C::STAGE;
         const lds_char* vb = kb + C::TILE;
-
         const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > wq0 + p.causal_shift);
 
-        // Two 32-key halves, each: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
-        // The reference decision is made per half, so the halves are independent
-        // steps of the same recurrence.
+        // S^T of both 32-key halves first: the MFMA pipe works through the
+        // second half while the first half's softmax runs on the VALU.
+        f32x16 s[2][C::NQB];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
-            f32x16 s[C::NQB];
 #pragma unroll
-            for (int qb = 0; qb < C::NQB; ++qb) s[qb] = f32x16{};
+            for (int qb = 0; qb < C::NQB; ++qb) s[kh][qb] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
                 const bf16x8 a = lds_b128(kb + k_off[ks] + kh * 32 * C::ROW);
 #pragma unroll
-                for (int qb = 0; qb < C::NQB; ++qb) s[qb] = mfma_bf16_32x32x16(a, qf[qb][ks], s[qb]);
+                for (int qb = 0; qb < C::NQB; ++qb) s[kh][qb] = mfma_bf16_32x32x16(a, qf[qb][ks], s[kh][qb]);
             }
+        }
 
+        // Per half: mask, online softmax, O^T += V^T P^T.  The reference
+        // decision is made per half, so the halves are two steps of the same
+        // recurrence.
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
             // Mask keys past Nk and, for causal problems, keys after each
             // query's diagonal.  Only tiles that straddle either edge pay.
             if (need_mask) {
@@ -250,17 +247,15 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                     const int lim = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - key0 - 32 * kh - 4 * g;
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        if (8 * (i >> 2) + (i & 3) > lim) s[qb][i] = -INFINITY;
+                        if (8 * (i >> 2) + (i & 3) > lim) s[kh][qb][i] = -INFINITY;
                 }
             }
 
             bf16x8 pb[C::NQB][2];
 #pragma unroll
             for (int qb = 0; qb < C::NQB; ++qb) {
-                float mx = s[qb][0];
-#pragma unroll
-                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[qb][i]);
-                mx = pair_max(mx) * p.c;                         // half-tile max, log2 units
+                f32x16& sv = s[kh][qb];
+                const float mx = pair_max(max16(sv)) * p.c;      // half-tile max, log2 units
                 const bool move = mx > mref[qb] + kRescaleLog2;  // false while nothing is visible
                 if (__builtin_amdgcn_ballot_w64(move) != 0) {
                     const float mnew = move ? mx : mref[qb];
@@ -271,20 +266,14 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                     for (int db = 0; db < C::DB; ++db) o[qb][db] *= alpha;
                 }
                 const float mb = (mref[qb] == -INFINITY) ? 0.f : mref[qb];
-                float rs = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float e = fast_exp2(fmaf(s[qb][i], p.c, -mb));
-                    s[qb][i] = e;
-                    rs += e;
-                }
-                l[qb] += rs;
+                for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(fmaf(sv[i], p.c, -mb));
+                l[qb] += sum16(sv);
 #pragma unroll
                 for (int h8 = 0; h8 < 2; ++h8) {
                     u32x4 pk;
 #pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2)
-                        pk[e2] = pack_bf16x2(s[qb][8 * h8 + 2 * e2], s[qb][8 * h8 + 2 * e2 + 1]);
+                    for (int e2 = 0; e2 < 4; ++e2) pk[e2] = pack_bf16x2(sv[8 * h8 + 2 * e2], sv[8 * h8 + 2 * e2 + 1]);
                     pb[qb][h8] = __builtin_bit_cast(bf16x8, pk);
                 }
             }
@@ -302,6 +291,12 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                 }
             }
         }
+    };
+
+    if (n_tiles > 0) issue_tile(0, 0);
+    for (int j = 0; j < n_tiles; j += 2) {
+        tile(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, j + 1);
     }
 
     // Epilogue: normalise once, stage O as bf16 in LDS, then write whole rows
