@@ -25,10 +25,10 @@
 //
 // K/V staging: the global loads go straight into LDS (global_load_lds_dwordx4,
 // 1 KiB per wave instruction, no staging registers), NSTAGE tiles deep.  LDS
-// rows are XOR swizzled in 16-byte units -- K by (row mod 16) (mod 8 at
-// d = 64), so the rows one ds_read_b128 touches hit distinct banks, V by
-// 2*(row mod 4), so the four rows one transposing read touches do -- and the
-// swizzle is realised by choosing which global 16 bytes each lane fetches.
+// rows are XOR swizzled in 16-byte units so that the rows one ds_read_b128
+// cycle (K) or one transposing-read cycle (V) touches hit distinct banks
+// (Bf16Cfg::kswz / vswz) -- and the swizzle is realised by choosing which
+// global 16 bytes each lane fetches.
 // All per-lane LDS and global offsets are loop invariant; a tile only adds
 // scalar bases.
 //
@@ -75,7 +75,15 @@ struct Bf16Cfg {
     static constexpr int RPC = 1024 / ROW;       // rows per 1 KiB chunk
     static constexpr int KS = D / 16;            // MFMA steps over d for S
     static constexpr int DB = D / 32;            // 32-wide blocks of d in O
-    static constexpr int KSW = UPR - 1;          // K swizzle mask (rows mod 16 or mod 8)
+    // LDS swizzles, in 16-byte units (LDS: 64 banks of 4 bytes, 256 B per cycle).
+    // K: the 16 rows one ds_read_b128 cycle touches must cover all 16 units:
+    //   256-byte rows (d=128) by row mod 16; 128-byte rows (d=64, two rows per
+    //   bank sweep) by (row/2) mod 8.
+    // V: the 4 rows x 64 bytes one transposing-read cycle touches must cover
+    //   all 16 units: XOR bits 2-3 of the unit with row mod 4 (d=128), or bit 2
+    //   with (row/2) mod 2 (d=64).
+    __device__ static constexpr int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+    __device__ static constexpr int vswz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
     static_assert(CHUNKS % NW == 0, "tile must split evenly over the waves");
     static_assert(RW == 32 || RW == 64, "32 or 64 query rows per wave");
 };
@@ -144,24 +152,24 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
 #pragma unroll
     for (int t = 0; t < C::CPW; ++t) {
         const int row = (w * C::CPW + t) * C::RPC + c_row;
-        dk_off[t] = row * C::ROW + ((c_su ^ (row & C::KSW)) << 4);
-        dv_off[t] = row * C::ROW + ((c_su ^ (2 * (row & 3))) << 4);
+        dk_off[t] = row * C::ROW + ((c_su ^ C::kswz(row)) << 4);
+        dv_off[t] = row * C::ROW + ((c_su ^ C::vswz(row)) << 4);
     }
     // K reads: row 32*kh + n, unit 2*ks + g, swizzled by row (kh adds 32 rows)
     uint32_t k_off[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = n * C::ROW + (((2 * ks + g) ^ (n & C::KSW)) << 4);
+    for (int ks = 0; ks < C::KS; ++ks) k_off[ks] = n * C::ROW + (((2 * ks + g) ^ C::kswz(n)) << 4);
     // V^T reads: lane (n, g) sources key row 4*g + (n%16)/4 (+8, +16*st) at
-    // d = 16*(n/16) + 4*(n%4) (+32*db).  The swizzle of d-block db depends on
-    // db only through db's low bit; db >= 2 adds a constant 8 units.
-    uint32_t v_off[2];
+    // d = 32*db + 16*(n/16) + 4*(n%4); one base per d-block (the row steps
+    // keep row mod 4 and are immediates).
+    uint32_t v_off[C::DB];
     {
         const int tr_row = 4 * g + ((n & 15) >> 2);
         const int tr_d = 16 * (n >> 4) + 4 * (n & 3);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int d = 32 * e + tr_d;
-            v_off[e] = tr_row * C::ROW + ((((d >> 3) ^ (2 * (tr_row & 3)))) << 4) + (d & 7) * 2;
+        for (int db = 0; db < C::DB; ++db) {
+            const int d = 32 * db + tr_d;
+            v_off[db] = tr_row * C::ROW + (((d >> 3) ^ C::vswz(tr_row)) << 4) + (d & 7) * 2;
         }
     }
 
@@ -186,8 +194,8 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
             for (int t = 0; t < C::CPW; ++t) {
                 const int row = (w * C::CPW + t) * C::RPC + c_row;
                 const int rc = min(row, last);
-                dma16(kb, rc * C::ROW + ((c_su ^ (row & C::KSW)) << 4), kdst + t * 1024);
-                dma16(vb, rc * C::ROW + ((c_su ^ (2 * (row & 3))) << 4), vdst + t * 1024);
+                dma16(kb, rc * C::ROW + ((c_su ^ C::kswz(row)) << 4), kdst + t * 1024);
+                dma16(vb, rc * C::ROW + ((c_su ^ C::vswz(row)) << 4), vdst + t * 1024);
             }
         }
     };
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                 const int st = 2 * kh + h8;                      // 16-key step within the tile
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
-                    const lds_char* vp = vb + v_off[db & 1] + (db >> 1) * 128 + 16 * st * C::ROW;
+                    const lds_char* vp = vb + v_off[db] + 16 * st * C::ROW;
                     const i16x4 lo = lds_tr16(vp);
                     const i16x4 hi = lds_tr16(vp + 8 * C::ROW);
                     const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                 val[0] = pack_bf16x2(o[qb][db][4 * i4 + 0] * inv, o[qb][db][4 * i4 + 1] * inv);
                 val[1] = pack_bf16x2(o[qb][db][4 * i4 + 2] * inv, o[qb][db][4 * i4 + 3] * inv);
                 *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-                    smem + row * C::ROW + ((u ^ (row & C::KSW)) << 4) + 8 * g) = val;
+                    smem + row * C::ROW + ((u ^ C::kswz(row)) << 4) + 8 * g) = val;
             }
         const int qrow = wq0 + 32 * qb + n;
         if (p.lse != nullptr && g == 0 && qrow < p.Nq) {
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         if (grow < p.Nq) {
             const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
                 smem + row * C::ROW + su * 16);
-            *reinterpret_cast<u32x4*>(Oh + (int64_t)grow * C::ROW + ((su ^ (row & C::KSW)) << 4)) = v;
+            *reinterpret_cast<u32x4*>(Oh + (int64_t)grow * C::ROW + ((su ^ C::kswz(row)) << 4)) = v;
         }
     }
 }

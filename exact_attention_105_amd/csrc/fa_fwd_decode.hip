@@ -97,19 +97,21 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int 
     for (int c = 0; c < kCH; ++c) {
         const int row = 4 * c + c_row;
         dk_off[c] = row * kROW + ((c_su ^ (row & 15)) << 4);
-        dv_off[c] = row * kROW + ((c_su ^ (2 * (row & 3))) << 4);
+        dv_off[c] = row * kROW + ((c_su ^ (4 * (row & 3))) << 4);
     }
     uint32_t k_off[kD / 16];
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) k_off[ks] = n * kROW + (((2 * ks + g) ^ (n & 15)) << 4);
-    uint32_t v_off[2];
+    // V rows are swizzled by 4*(row mod 4) units: the 4 rows x 64 bytes of one
+    // transposing-read cycle then cover all 64 banks.
+    uint32_t v_off[kD / 32];
     {
         const int tr_row = 4 * g + ((n & 15) >> 2);
         const int tr_d = 16 * (n >> 4) + 4 * (n & 3);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int d = 32 * e + tr_d;
-            v_off[e] = tr_row * kROW + (((d >> 3) ^ (2 * (tr_row & 3))) << 4) + (d & 7) * 2;
+        for (int db = 0; db < kD / 32; ++db) {
+            const int d = 32 * db + tr_d;
+            v_off[db] = tr_row * kROW + (((d >> 3) ^ (4 * (tr_row & 3))) << 4) + (d & 7) * 2;
         }
     }
 
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int 
                 const int row = 4 * c + c_row;
                 const int rc = min(row, last);
                 dma16(kb, rc * kROW + ((c_su ^ (row & 15)) << 4), kdst + c * 1024);
-                dma16(vb, rc * kROW + ((c_su ^ (2 * (row & 3))) << 4), vdst + c * 1024);
+                dma16(vb, rc * kROW + ((c_su ^ (4 * (row & 3))) << 4), vdst + c * 1024);
             }
         }
     };
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int 
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
             for (int db = 0; db < kD / 32; ++db) {
-                const lds_char* vp = vb + v_off[db & 1] + (db >> 1) * 128 + 16 * h8 * kROW;
+                const lds_char* vp = vb + v_off[db] + 16 * h8 * kROW;
                 const i16x4 lo = lds_tr16(vp);
                 const i16x4 hi = lds_tr16(vp + 8 * kROW);
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
