@@ -62,14 +62,20 @@ def cpu_baseline(cfg, x, budget_s: float):
     rng = np.random.default_rng(12345)
     total_rows = cfg.B * cfg.Hq * cfg.Nq
     threads = oracle.num_threads()
-    # calibrate on a small batch, then run one batch sized to the budget
+    # calibrate: grow a batch until it takes a tenth of the budget (a tiny
+    # batch is dominated by thread start-up and under-estimates the rate),
+    # then run one batch sized to the whole budget
     n0 = min(total_rows, max(8, threads * 2))
-    rows = np.sort(rng.choice(total_rows, size=n0, replace=False))
-    t0 = time.perf_counter()
-    oracle.attention(x["q"], x["k"], x["v"], causal=cfg.causal, scale=cfg.scale, dtype=cfg.dtype,
-                     descale=x.get("descale"), rows=rows)
-    dt0 = time.perf_counter() - t0
-    n = int(min(total_rows, max(n0, n0 * max(budget_s - dt0, 0.0) / max(dt0, 1e-6))))
+    while True:
+        rows = np.sort(rng.choice(total_rows, size=n0, replace=False))
+        t0 = time.perf_counter()
+        oracle.attention(x["q"], x["k"], x["v"], causal=cfg.causal, scale=cfg.scale, dtype=cfg.dtype,
+                         descale=x.get("descale"), rows=rows)
+        dt0 = time.perf_counter() - t0
+        if dt0 >= 0.1 * budget_s or n0 >= total_rows:
+            break
+        n0 = min(total_rows, n0 * 4)
+    n = int(min(total_rows, max(n0, n0 * budget_s / max(dt0, 1e-6))))
     rows = np.sort(rng.choice(total_rows, size=n, replace=False))
     t0 = time.perf_counter()
     oracle.attention(x["q"], x["k"], x["v"], causal=cfg.causal, scale=cfg.scale, dtype=cfg.dtype,
