@@ -1,17 +1,17 @@
 // Fused exact-attention forward pass, bfloat16 inputs, head dim 64 or 128, gfx950.
 //
-// One workgroup owns BM = 256 query rows of one (batch, query head) and
+// One workgroup owns BM = 128 query rows of one (batch, query head) and
 // streams the key/value rows of that head's key/value head through LDS in
 // tiles of BN = 64 keys ("FlashAttention (DE)", systems-analysis.info,
 // section "Tiling und blockweise Verarbeitung").  Each of the four waves owns
-// 64 query rows and keeps, per row, a running maximum and a running sum of
+// 32 query rows and keeps, per row, a running maximum and a running sum of
 // exponentials (same page, section "Online-Softmax-Berechnung"); scores,
 // mask, softmax and the product with V never leave the chip (same page,
 // section "Zusammenfassen von Operationen in einem CUDA-Kernel").  Only O and
 // the per-row log-sum-exp are written.
 //
 // Matrix layout (gfx950 MFMA 32x32x16 bf16, see fa_device.hpp), per wave and
-// per 32-query block qb of its 64 rows:
+// per 32-query block qb of its rows:
 //   S^T = K Q^T    : A = K rows from LDS (ds_read_b128), B = Q rows held in
 //                    registers for the whole key loop.  Lane l ends up with
 //                    the scores of query l%32 against 16 of every 32 keys.
@@ -19,9 +19,11 @@
 //                    transposing read ds_read_b64_tr_b16 (16 lanes read a
 //                    4-key x 16-d block; each lane receives one d column of
 //                    4 keys), B = P straight from the score registers.
-// Every K and V^T fragment read from LDS feeds two MFMAs (the wave's two
-// query blocks), which halves LDS traffic per flop against 32 rows per wave;
-// with 32 rows per wave the LDS reads alone take about as long as the MFMAs.
+// 32 rows per wave keep the registers at about 100 VGPRs, so two workgroups
+// (eight waves) share a CU and one workgroup's softmax overlaps the other's
+// MFMAs.  64 rows per wave (FA_BF16_RW128 / FA_BF16_RW64 = 64) would feed
+// every K and V^T fragment read from LDS to two MFMAs, but needs the
+// accumulators in AGPRs and runs one workgroup per CU; measured slower.
 //
 // K/V staging: the global loads go straight into LDS (global_load_lds_dwordx4,
 // 1 KiB per wave instruction, no staging registers), NSTAGE tiles deep.  LDS
