@@ -2,7 +2,7 @@
 //
 // One workgroup owns BM = 128 query rows of one (batch, query head) and
 // streams the key/value rows of that head's key/value head through LDS in
-// tiles of BN = 64 keys ("FlashAttention (DE)", systems-analysis.info,
+// tiles of BN = 32 keys ("FlashAttention (DE)", systems-analysis.info,
 // section "Tiling und blockweise Verarbeitung").  Each of the four waves owns
 // 32 query rows and keeps, per row, a running maximum and a running sum of
 // exponentials (same page, section "Online-Softmax-Berechnung"); scores,
@@ -19,14 +19,18 @@
 //                    transposing read ds_read_b64_tr_b16 (16 lanes read a
 //                    4-key x 16-d block; each lane receives one d column of
 //                    4 keys), B = P straight from the score registers.
-// 32 rows per wave keep the registers at about 100 VGPRs, so two workgroups
-// (eight waves) share a CU and one workgroup's softmax overlaps the other's
-// MFMAs.  64 rows per wave (FA_BF16_RW128 / FA_BF16_RW64 = 64) would feed
-// every K and V^T fragment read from LDS to two MFMAs, but needs the
-// accumulators in AGPRs and runs one workgroup per CU; measured slower.
+// Two workgroups (eight waves) share a CU, so one wave's softmax overlaps
+// the other's MFMAs on each SIMD.  Short 32-key tiles make the waves
+// alternate between MFMA and VALU phases often, which measured faster than
+// 64-key tiles at the same occupancy (FA_BF16_BN); deeper LDS pipelines
+// (FA_BF16_NSTAGE) and more workgroups per CU (FA_BF16_OCC) did not help.
+// 64 rows per wave (FA_BF16_RW128 / FA_BF16_RW64 = 64) would feed every K
+// and V^T fragment read from LDS to two MFMAs, but needs the accumulators in
+// AGPRs and runs one workgroup per CU; measured slower.
 //
 // K/V staging: the global loads go straight into LDS (global_load_lds_dwordx4,
-// 1 KiB per wave instruction, no staging registers), NSTAGE tiles deep.  LDS
+// 1 KiB per wave instruction, no staging registers), NSTAGE tiles deep, with
+// one barrier per tile.  LDS
 // rows are XOR swizzled in 16-byte units so that the rows one ds_read_b128
 // cycle (K) or one transposing-read cycle (V) touches hit distinct banks
 // (Bf16Cfg::kswz / vswz) -- and the swizzle is realised by choosing which
@@ -51,6 +55,15 @@ namespace fa {
 
 constexpr float kRescaleLog2 = 8.0f;
 
+#ifndef FA_BF16_BN
+#define FA_BF16_BN 32
+#endif
+#ifndef FA_BF16_NSTAGE
+#define FA_BF16_NSTAGE 2
+#endif
+#ifndef FA_BF16_OCC
+#define FA_BF16_OCC 2
+#endif
 #ifndef FA_BF16_RW128
 #define FA_BF16_RW128 32     // query rows per wave at d = 128 (32 or 64)
 #endif
@@ -58,15 +71,33 @@ constexpr float kRescaleLog2 = 8.0f;
 #define FA_BF16_RW64 32      // query rows per wave at d = 64 (32 or 64)
 #endif
 
+// Wait until at most `ahead` tiles' worth of this wave's LDS copies (PER
+// instructions each) are outstanding, ahead in 0..MAXA.
+template <int PER, int MAXA>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+    if (MAXA >= 2 && ahead >= 2) FA_WAIT_VMCNT(2 * PER);
+    else if (MAXA >= 1 && ahead >= 1) FA_WAIT_VMCNT(PER);
+    else FA_WAIT_VMCNT(0);
+}
+
+// Workgroup barrier without a memory fence (the copies are awaited with
+// explicit vmcnt waits); the asm keeps the compiler from moving LDS accesses
+// across it, and lgkmcnt(0) retires this wave's LDS reads of the stage the
+// next copies will overwrite.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int D>
 struct Bf16Cfg {
     static constexpr int NW = 4;                 // waves per workgroup
     static constexpr int RW = D == 128 ? FA_BF16_RW128 : FA_BF16_RW64;  // query rows per wave
     static constexpr int NQB = RW / 32;          // 32-row query blocks per wave
     static constexpr int BM = RW * NW;           // query rows per workgroup
-    static constexpr int BN = 64;                // keys per K/V tile
-    static constexpr int NSTAGE = 2;             // K/V tiles resident in LDS
-    static constexpr int OCC = RW == 32 ? 2 : 1; // workgroups per CU the registers allow
+    static constexpr int BN = FA_BF16_BN;        // keys per K/V tile
+    static constexpr int KH = BN / 32;           // 32-key halves per tile
+    static constexpr int NSTAGE = FA_BF16_NSTAGE; // K/V tiles resident in LDS
+    static constexpr int OCC = RW == 32 ? FA_BF16_OCC : 1; // workgroups per CU
     static constexpr int ROW = D * 2;            // bytes of one K or V row in LDS
     static constexpr int UPR = D / 8;            // 16-byte units per row
     static constexpr int TILE = BN * ROW;        // bytes of one K (or V) tile
@@ -88,6 +119,7 @@ struct Bf16Cfg {
     __device__ static constexpr int vswz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
     static_assert(CHUNKS % NW == 0, "tile must split evenly over the waves");
     static_assert(RW == 32 || RW == 64, "32 or 64 query rows per wave");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 LDS stages");
 };
 
 template <int D, bool CAUSAL>
@@ -218,9 +250,11 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
     // loop-invariant per-lane register plus an immediate offset.
     auto tile = [&](auto stage_c, int j) {
         constexpr int STG = decltype(stage_c)::value;
-        FA_WAIT_VMCNT(0);                       // this wave's copies of tile j landed
-        __syncthreads();                        // ... and every other wave's
-        if (j + 1 < n_tiles) issue_tile(j + 1, STG ^ 1);
+        // this wave's copies of tile j landed (those of the next tiles may
+        // still be in flight), then every other wave's
+        wait_tiles<2 * C::CPW, C::NSTAGE - 2>(min(C::NSTAGE - 2, n_tiles - 1 - j));
+        wg_barrier();
+        if (j + C::NSTAGE - 1 < n_tiles) issue_tile(j + C::NSTAGE - 1, (STG + C::NSTAGE - 1) % C::NSTAGE);
 
         const int key0 = j * C::BN;
         if (key0 >= wkend) return;              // every key of this tile is hidden from this wave
@@ -228,11 +262,12 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         const lds_char* vb = kb + C::TILE;
         const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > wq0 + p.causal_shift);
 
-        // S^T of both 32-key halves first: the MFMA pipe works through the
-        // second half while the first half's softmax runs on the VALU.
-        f32x16 s[2][C::NQB];
+        // S^T of every 32-key half of the tile first (64-key tiles: the MFMA
+        // pipe works through the second half while the first half's softmax
+        // runs on the VALU).
+        f32x16 s[C::KH][C::NQB];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
+        for (int kh = 0; kh < C::KH; ++kh) {
 #pragma unroll
             for (int qb = 0; qb < C::NQB; ++qb) s[kh][qb] = f32x16{};
 #pragma unroll
@@ -247,7 +282,7 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         // decision is made per half, so the halves are two steps of the same
         // recurrence.
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
+        for (int kh = 0; kh < C::KH; ++kh) {
             // Mask keys past Nk and, for causal problems, keys after each
             // query's diagonal.  Only tiles that straddle either edge pay.
             if (need_mask) {
@@ -303,10 +338,14 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         }
     };
 
-    if (n_tiles > 0) issue_tile(0, 0);
-    for (int j = 0; j < n_tiles; j += 2) {
+#pragma unroll
+    for (int t = 0; t < C::NSTAGE - 1; ++t)
+        if (t < n_tiles) issue_tile(t, t);
+    for (int j = 0; j < n_tiles; j += C::NSTAGE) {
         tile(std::integral_constant<int, 0>{}, j);
-        if (j + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, j + 1);
+        if (j + 1 < n_tiles) tile(std::integral_constant<int, 1 % C::NSTAGE>{}, j + 1);
+        if (C::NSTAGE > 2 && j + 2 < n_tiles) tile(std::integral_constant<int, 2 % C::NSTAGE>{}, j + 2);
+        if (C::NSTAGE > 3 && j + 3 < n_tiles) tile(std::integral_constant<int, 3 % C::NSTAGE>{}, j + 3);
     }
 
     // Epilogue: normalise once, stage O as bf16 in LDS, then write whole rows
