@@ -54,6 +54,10 @@
 namespace fa {
 
 constexpr float kRescaleLog2 = 8.0f;
+// Reference of a row that has seen no visible key: finite, so the first move
+// gives alpha = exp2(kNoRef - m) = 0 and an unmoved row exp2(0) = 1 without
+// special cases; any visible score moves it.
+constexpr float kNoRef = -1.0e30f;
 
 #ifndef FA_BF16_BN
 #define FA_BF16_BN 32
@@ -152,12 +156,16 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
 
     // Keys this workgroup needs: all of them, or (causal) up to the last
     // visible key of its last row; key tiles beyond are skipped entirely.
+    // (The bounds are workgroup- or wave-uniform; readfirstlane keeps them,
+    // and the loop control built on them, in scalar registers -- the integer
+    // division behind the head mapping is computed on the vector ALU.)
     int kend = p.Nk;
     if (CAUSAL) kend = min(kend, max(q0 + C::BM + p.causal_shift, 0));
-    const int n_tiles = (kend + C::BN - 1) / C::BN;
+    const int n_tiles = __builtin_amdgcn_readfirstlane((kend + C::BN - 1) / C::BN);
     // Keys this wave needs (its other tiles only take part in the copies).
     int wkend = p.Nk;
     if (CAUSAL) wkend = min(wkend, max(wq0 + C::RW + p.causal_shift, 0));
+    wkend = __builtin_amdgcn_readfirstlane(wkend);
 
     // Q rows of this lane as MFMA B operands, resident for the whole loop.
     bf16x8 qf[C::NQB][C::KS];
@@ -236,12 +244,14 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
 
     f32x16 o[C::NQB][C::DB];
     float mref[C::NQB];      // exponent reference per row, log2 units
+    float thr[C::NQB];       // raw score above which the reference must move
     float l[C::NQB];         // this lane's part of the row sums
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) o[qb][db] = f32x16{};
-        mref[qb] = -INFINITY;
+        mref[qb] = kNoRef;
+        thr[qb] = -INFINITY;     // the first visible score sets the reference
         l[qb] = 0.f;
     }
 
@@ -300,19 +310,24 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
 #pragma unroll
             for (int qb = 0; qb < C::NQB; ++qb) {
                 f32x16& sv = s[kh][qb];
-                const float mx = pair_max(max16(sv)) * p.c;      // half-tile max, log2 units
-                const bool move = mx > mref[qb] + kRescaleLog2;  // false while nothing is visible
-                if (__builtin_amdgcn_ballot_w64(move) != 0) {
+                // Each lane compares the maximum of its own 16 raw scores with
+                // the threshold; only when some lane passes it does the wave
+                // form the row maxima and move references (rare after the
+                // first tile).
+                const float lm = max16(sv);
+                if (__builtin_amdgcn_ballot_w64(lm > thr[qb]) != 0) {
+                    const float mx = pair_max(lm) * p.c;            // row max of the tile, log2 units
+                    const bool move = mx > mref[qb] + kRescaleLog2;
                     const float mnew = move ? mx : mref[qb];
-                    const float alpha = move ? ((mref[qb] == -INFINITY) ? 0.f : fast_exp2(mref[qb] - mnew)) : 1.f;
+                    const float alpha = fast_exp2(mref[qb] - mnew);  // 0 at the first move, 1 if unmoved
                     mref[qb] = mnew;
+                    thr[qb] = (mnew + kRescaleLog2) / p.c;
                     l[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < C::DB; ++db) o[qb][db] *= alpha;
                 }
-                const float mb = (mref[qb] == -INFINITY) ? 0.f : mref[qb];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(fmaf(sv[i], p.c, -mb));
+                for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(fmaf(sv[i], p.c, -mref[qb]));
                 l[qb] += sum16(sv);
 #pragma unroll
                 for (int h8 = 0; h8 < 2; ++h8) {
