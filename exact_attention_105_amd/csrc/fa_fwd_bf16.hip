@@ -66,7 +66,7 @@ constexpr float kNoRef = -1.0e30f;
 #define FA_BF16_NSTAGE 2
 #endif
 #ifndef FA_BF16_OCC
-#define FA_BF16_OCC 2
+#define FA_BF16_OCC 3
 #endif
 #ifndef FA_BF16_RW128
 #define FA_BF16_RW128 32     // query rows per wave at d = 128 (32 or 64)
@@ -264,10 +264,12 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         // still be in flight), then every other wave's
         wait_tiles<2 * C::CPW, C::NSTAGE - 2>(min(C::NSTAGE - 2, n_tiles - 1 - j));
         wg_barrier();
-        if (j + C::NSTAGE - 1 < n_tiles) issue_tile(j + C::NSTAGE - 1, (STG + C::NSTAGE - 1) % C::NSTAGE);
 
         const int key0 = j * C::BN;
-        if (key0 >= wkend) return;              // every key of this tile is hidden from this wave
+        if (key0 >= wkend) {                    // every key of this tile is hidden from this wave
+            if (j + C::NSTAGE - 1 < n_tiles) issue_tile(j + C::NSTAGE - 1, (STG + C::NSTAGE - 1) % C::NSTAGE);
+            return;
+        }
         const lds_char* kb = smem + STG * C::STAGE;
         const lds_char* vb = kb + C::TILE;
         const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > wq0 + p.causal_shift);
@@ -276,6 +278,10 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         // pipe works through the second half while the first half's softmax
         // runs on the VALU).
         f32x16 s[C::KH][C::NQB];
+        // MFMA blocks run at raised wave priority, so a co-resident wave in
+        // its softmax phase issues its VALU work around them.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kh = 0; kh < C::KH; ++kh) {
 #pragma unroll
@@ -287,6 +293,11 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                 for (int qb = 0; qb < C::NQB; ++qb) s[kh][qb] = mfma_bf16_32x32x16(a, qf[qb][ks], s[kh][qb]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        // The next tile's copies go out after the score MFMAs, in the wait
+        // before their results can be read.
+        if (j + C::NSTAGE - 1 < n_tiles) issue_tile(j + C::NSTAGE - 1, (STG + C::NSTAGE - 1) % C::NSTAGE);
 
         // Per half: mask, online softmax, O^T += V^T P^T.  The reference
         // decision is made per half, so the halves are two steps of the same
@@ -337,6 +348,8 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                     pb[qb][h8] = __builtin_bit_cast(bf16x8, pk);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int h8 = 0; h8 < 2; ++h8) {
                 const int st = 2 * kh + h8;                      // 16-key step within the tile
@@ -350,6 +363,8 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                     for (int qb = 0; qb < C::NQB; ++qb) o[qb][db] = mfma_bf16_32x32x16(a, pb[qb][h8], o[qb][db]);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 
