@@ -24,11 +24,12 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-# Per-source additions.  The bf16 prefill kernel schedules for instruction
-# level parallelism (measured faster than the default occupancy-driven
-# schedule, at the same three waves per SIMD).
+# Per-source additions.  The prefill kernels schedule for instruction level
+# parallelism (measured faster than the default occupancy-driven schedule, at
+# the same three waves per SIMD).
 SOURCE_FLAGS = {
     "fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "fa_fwd_fp8.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 

@@ -33,6 +33,9 @@ namespace fa {
 
 constexpr float kP8Offset = 6.0f;   // log2 of the factor carried by the exponentials
 constexpr float kP8Slack = 2.0f;    // log2 growth of the max tolerated before rescaling
+// Reference of a row that has seen no visible key: finite, so the first move
+// gives alpha = exp2(kNoRef8 - m) = 0 and an unmoved row exp2(0) = 1.
+constexpr float kNoRef8 = -1.0e30f;
 
 struct Fp8Cfg {
     static constexpr int D = 128;
@@ -90,11 +93,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
     const char* Kh = reinterpret_cast<const char*>(p.k) + ((int64_t)(b * p.Hkv + hkv) * p.Nk) * D;
     const char* Vh = reinterpret_cast<const char*>(p.v) + ((int64_t)(b * p.Hkv + hkv) * p.Nk) * D;
 
+    // (readfirstlane keeps these uniform bounds, and the loop control built
+    // on them, in scalar registers)
     int kend = p.Nk;
     if (CAUSAL) kend = min(kend, max(q0 + C::BM + p.causal_shift, 0));
-    const int n_tiles = (kend + C::BN - 1) / C::BN;
+    const int n_tiles = __builtin_amdgcn_readfirstlane((kend + C::BN - 1) / C::BN);
     int wkend = p.Nk;
     if (CAUSAL) wkend = min(wkend, max(wq0 + 32 + p.causal_shift, 0));
+    wkend = __builtin_amdgcn_readfirstlane(wkend);
 
     // Q as B operands: k-step ks covers d = 64*ks + 32*g + [0, 32).
     i32x8 qf[2];
@@ -170,7 +176,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
     f32x16 o[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
-    float mref = -INFINITY;   // exponent reference of this row, log2 units
+    float mref = kNoRef8;     // exponent reference of this row, log2 units
+    float thr = -INFINITY;    // raw score above which the reference must move
     float l = 0.f;            // this lane's part of the row sum, times 2^kP8Offset
 
     if (n_tiles > 0) issue_tile(0, 0);
@@ -179,13 +186,19 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
         const int stage = j & 1;
         FA_WAIT_VMCNT(0);
         __syncthreads();
-        if (j + 1 < n_tiles) issue_tile(j + 1, stage ^ 1);
 
         const int key0 = j * C::BN;
-        if (key0 >= wkend) continue;
+        if (key0 >= wkend) {
+            if (j + 1 < n_tiles) issue_tile(j + 1, stage ^ 1);
+            continue;
+        }
         const lds_char* kb = smem + stage * C::STAGE;
         const lds_char* vb = kb + C::TILE;
 
+        // MFMA blocks run at raised wave priority, so a co-resident wave in
+        // its softmax phase issues its VALU work around them.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
         f32x16 s[2];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
@@ -199,6 +212,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
                 s[kh] = mfma_fp8_32x32x64(a, qf[ks], s[kh]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        // the next tile's copies go out in the wait before the scores can be read
+        if (j + 1 < n_tiles) issue_tile(j + 1, stage ^ 1);
 
         const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > wq0 + p.causal_shift);
         if (need_mask) {
@@ -210,32 +227,27 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
                     if (32 * kh + 8 * (i >> 2) + (i & 3) > lim) s[kh][i] = -INFINITY;
         }
 
-        float mx = s[0][0];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kh][i]);
-        mx = pair_max(mx) * p.c;
-        const bool move = mx > mref + kP8Slack;
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        // Each lane compares the maximum of its own raw scores with the
+        // threshold; only when some lane passes it does the wave form the row
+        // maxima and move references.
+        const float lm = fmaxf(max16(s[0]), max16(s[1]));
+        if (__builtin_amdgcn_ballot_w64(lm > thr) != 0) {
+            const float mx = pair_max(lm) * p.c;
+            const bool move = mx > mref + kP8Slack;
             const float mnew = move ? mx : mref;
-            const float alpha = move ? ((mref == -INFINITY) ? 0.f : fast_exp2(mref - mnew)) : 1.f;
+            const float alpha = fast_exp2(mref - mnew);   // 0 at the first move, 1 if unmoved
             mref = mnew;
+            thr = (mnew + kP8Slack) / p.c;
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
         }
-        const float off = kP8Offset - ((mref == -INFINITY) ? 0.f : mref);
-        float rs = 0.f;
+        const float off = kP8Offset - mref;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float e = fast_exp2(fmaf(s[kh][i], p.c, off));
-                s[kh][i] = e;
-                rs += e;
-            }
-        l += rs;
+            for (int i = 0; i < 16; ++i) s[kh][i] = fast_exp2(fmaf(s[kh][i], p.c, off));
+        l += sum16(s[0]) + sum16(s[1]);
 
         i32x8 pb;
 #pragma unroll
@@ -244,6 +256,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
             for (int q4 = 0; q4 < 4; ++q4)
                 pb[4 * kh + q4] = (int)pack_fp8x4(s[kh][4 * q4], s[kh][4 * q4 + 1], s[kh][4 * q4 + 2], s[kh][4 * q4 + 3]);
 
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
             i32x8 a;
@@ -255,6 +269,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
             }
             o[db] = mfma_fp8_32x32x64(a, pb, o[db]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
     }
 
     // Epilogue: normalise, stage O as bf16 in LDS, coalesced 16-byte stores.
