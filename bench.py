@@ -33,25 +33,38 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s on 1 MI355X (bf16/fp8) and % of MFMA peak"
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
+def kernel_source(cfg) -> str:
+    """The source file of the kernel that runs this workload."""
+    if cfg.dtype == "e4m3":
+        return "fa_fwd_fp8.hip"
+    if cfg.d == 128 and cfg.Nq <= 16:
+        return "fa_fwd_decode.hip"
+    return "fa_fwd_bf16.hip"
+
+
+def kernel_source_hash(cfg) -> str:
+    """Hash of what the workload's kernel is compiled from: its source file,
+    the shared device header and that file's extra compiler flags."""
+    from exact_attention_105_amd import build as _build
+    src = kernel_source(cfg)
     csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+    h = hashlib.sha256()
+    for f in (src, "fa_device.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    h.update(" ".join(_build.HIPCC_FLAGS + _build.SOURCE_FLAGS.get(src, [])).encode())
     return h.hexdigest()[:16]
 
 
-def load_traffic(cfg_name: str, launches_bytes: float):
+def load_traffic(cfg):
     """HBM traffic per launch from the committed counter summary, if it was
     taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{cfg_name}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(cfg):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -111,6 +124,33 @@ def copy_calibration(args):
                       "GB_per_s": 2 * n * 4 / dt / 1e9}), flush=True)
 
 
+def gemm_reference(args):
+    """Context for the MFMA roofline: a large vendor-library bf16 GEMM
+    (torch.matmul, hipBLASLt on ROCm) timed the same way on the same GPU --
+    what dense MFMA work sustains under this GPU's clock and power limits."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = args.gemm_reference
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(args.warmup):
+        c = a @ b
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        c = a @ b
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"gemm_reference": f"bf16 torch.matmul {n}x{n}x{n}", "ms": ms, "TFLOP/s": tflops,
+                      "frac_of_peak": tflops / PEAK_TFLOPS["bf16"], "steps": args.steps}), flush=True)
+    del c
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,12 +159,17 @@ def main():
     ap.add_argument("--config", default="long16k_causal")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 to skip)")
+    ap.add_argument("--gemm-reference", type=int, default=0,
+                    help="instead of attention, time a bf16 n x n x n torch.matmul (vendor GEMM context)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.copy_bytes > 0:
         copy_calibration(args)
+        return
+    if args.gemm_reference > 0:
+        gemm_reference(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
@@ -178,7 +223,7 @@ def main():
         peak = PEAK_TFLOPS[cfg.dtype]
         roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": tflops / peak}
-    roof["traffic"] = load_traffic(cfg.name, cfg.algorithmic_bytes)
+    roof["traffic"] = load_traffic(cfg)
     roof["kernel_ms"] = ms
 
     result = {
@@ -189,7 +234,7 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Nq": cfg.Nq,
                    "Nk": cfg.Nk, "d": cfg.d, "causal": cfg.causal, "flops_per_step": cfg.flops,
                    "algorithmic_bytes_per_step": cfg.algorithmic_bytes,
-                   "kernel_source_hash": kernel_source_hash()},
+                   "kernel_source_hash": kernel_source_hash(cfg)},
         "roofline": roof,
         "wall_s_timed": wall,
     }

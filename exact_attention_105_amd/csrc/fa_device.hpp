@@ -118,6 +118,42 @@ __device__ __forceinline__ void head_of(const FwdParams& p, int x, int& b, int& 
     hq = hkv * p.group + gi;
 }
 
+// Workgroup -> (batch, query head, key/value head, query tile) for the
+// prefill kernels.  The hardware hands workgroups to the 8 XCDs round-robin
+// (id mod 8).
+//  * Causal problems: consecutive ids walk the heads first (head_of), the
+//    query tiles heaviest first, so every head's long rows start at the
+//    beginning of the launch (longest-first scheduling; the tail is made of
+//    the shortest tiles).
+//  * Non-causal problems, when B*Hkv is a multiple of 8: XCD x owns the
+//    key/value heads congruent to x mod 8 and walks them one at a time --
+//    the query heads of a key/value head next to each other, each head's
+//    query tiles consecutively -- so the workgroups resident on an XCD stream
+//    the same keys and values through its L2 together.  (For causal problems
+//    this order cut the fetched bytes about 8x but lost more to the late
+//    start of the last heads' long rows than it gained.)
+template <bool CAUSAL>
+__device__ __forceinline__ void tile_of(const FwdParams& p, int bid, int& b, int& hq, int& hkv, int& qt) {
+    const int kvh = p.B * p.Hkv;
+    int t_ord;
+    if (!CAUSAL && (kvh & 7) == 0) {
+        const int xcd = bid & 7;
+        const int L = bid >> 3;
+        const int hl = L / p.n_qtiles;          // head index within this XCD's share
+        t_ord = L - hl * p.n_qtiles;
+        const int kg = hl / p.group;
+        const int gi = hl - kg * p.group;
+        const int kvflat = xcd + 8 * kg;
+        b = kvflat / p.Hkv;
+        hkv = kvflat - b * p.Hkv;
+        hq = hkv * p.group + gi;
+    } else {
+        t_ord = bid / p.n_heads;
+        head_of(p, bid - t_ord * p.n_heads, b, hq, hkv);
+    }
+    qt = CAUSAL ? (p.n_qtiles - 1 - t_ord) : t_ord;
+}
+
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 

@@ -139,14 +139,9 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
     const int n = lane & 31;     // query column owned by this lane (in each 32-row block)
     const int g = lane >> 5;     // which half of the 32x32 block's rows
 
-    // Workgroup -> (head, query tile).  Consecutive workgroup ids walk the
-    // heads first, so all heads progress through their query tiles together;
-    // causal problems take the most expensive (last) query tiles first.
-    const int head_x = blockIdx.x % p.n_heads;
-    const int t_ord = blockIdx.x / p.n_heads;
-    const int qt = CAUSAL ? (p.n_qtiles - 1 - t_ord) : t_ord;
-    int b, hq, hkv;
-    head_of(p, head_x, b, hq, hkv);
+    // Workgroup -> (head, query tile), XCD-aware (tile_of in fa_device.hpp).
+    int b, hq, hkv, qt;
+    tile_of<CAUSAL>(p, blockIdx.x, b, hq, hkv, qt);
     const int q0 = qt * C::BM;
     const int wq0 = q0 + w * C::RW;              // first row of this wave
 

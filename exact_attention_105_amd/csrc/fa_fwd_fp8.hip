@@ -80,11 +80,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
     const int n = lane & 31;
     const int g = lane >> 5;
 
-    const int head_x = blockIdx.x % p.n_heads;
-    const int t_ord = blockIdx.x / p.n_heads;
-    const int qt = CAUSAL ? (p.n_qtiles - 1 - t_ord) : t_ord;
-    int b, hq, hkv;
-    head_of(p, head_x, b, hq, hkv);
+    // Workgroup -> (head, query tile), XCD-aware (tile_of in fa_device.hpp).
+    int b, hq, hkv, qt;
+    tile_of<CAUSAL>(p, blockIdx.x, b, hq, hkv, qt);
     const int q0 = qt * C::BM;
     const int wq0 = q0 + w * 32;
     const int qrow = wq0 + n;
