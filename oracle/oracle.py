@@ -12,7 +12,10 @@ query rows).  This wrapper only marshals numpy arrays into that library:
   or by the online-softmax recurrence (same page, section
   "Online-Softmax-Berechnung") when ``block_keys > 0``;
 * ``probs_row``   -- one materialised row of P;
-* ``decode``      -- the oracle's own bfloat16 / OCP-E4M3 decoders.
+* ``decode``      -- the oracle's own bfloat16 / OCP-E4M3 decoders;
+* ``rotate``, ``quantize_e4m3``, ``e4m3_encode`` -- the random-sign Hadamard
+  rotation and per-tensor FP8 quantisation of page "FlashAttention-3 (DE)",
+  systems-analysis.ru, technical innovation 3 (``rotate_oracle.c``).
 
 Inputs are the exact bytes the GPU receives: ``uint16`` arrays holding
 bfloat16 bit patterns, ``uint8`` arrays holding E4M3 codes (plus per-tensor
@@ -28,6 +31,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
+_ROT_SRC = os.path.join(_HERE, "rotate_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 DTYPES = {"bf16": 0, "e4m3": 1, "f64": 2}
@@ -36,12 +40,12 @@ _NP = {"bf16": np.uint16, "e4m3": np.uint8, "f64": np.float64}
 _default = None
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
-    """Compile the oracle C source into a shared library with gcc (IEEE semantics)."""
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH, rot_src: str = _ROT_SRC) -> str:
+    """Compile the oracle C sources into a shared library with gcc (IEEE semantics)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+               "-fno-fast-math", "-ffp-contract=off", src, rot_src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out
@@ -64,6 +68,15 @@ class OracleLib:
         lib.oracle_decode.argtypes = [vp, ctypes.c_int, ctypes.c_double, i64, dp]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_rotate.restype = ctypes.c_int
+        lib.oracle_rotate.argtypes = [vp, ctypes.c_int, i64, i64, ctypes.POINTER(ctypes.c_uint32),
+                                      ctypes.c_int, dp]
+        lib.oracle_quantize_e4m3.restype = None
+        lib.oracle_quantize_e4m3.argtypes = [dp, i64, dp, ctypes.POINTER(ctypes.c_uint8)]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_hadamard_entry.restype = ctypes.c_double
+        lib.oracle_hadamard_entry.argtypes = [i64, i64]
         self.lib = lib
         self.path = path
 
@@ -80,12 +93,25 @@ class OracleLib:
     def num_threads(self):
         return int(self.lib.oracle_num_threads())
 
+    def rotate(self, x, *, signs=None, rotate=True):
+        return _rotate(self.lib, x, signs, rotate)
+
+    def quantize_e4m3(self, y):
+        return _quantize(self.lib, y)
+
+    def e4m3_encode(self, v):
+        return int(self.lib.oracle_e4m3_encode(float(v)))
+
+    def hadamard_entry(self, i, j):
+        return float(self.lib.oracle_hadamard_entry(int(i), int(j)))
+
 
 def default() -> OracleLib:
-    """The oracle built from attn_oracle.c (rebuilt when the source is newer)."""
+    """The oracle built from its C sources (rebuilt when a source is newer)."""
     global _default
     if _default is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        newest = max(os.path.getmtime(_SRC), os.path.getmtime(_ROT_SRC))
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
             build(force=True)
         _default = OracleLib(_LIB_PATH)
     return _default
@@ -200,3 +226,69 @@ def decode(codes: np.ndarray, dtype: str, descale: float = 1.0) -> np.ndarray:
 def num_threads() -> int:
     """OpenMP threads the oracle will use (OMP_NUM_THREADS, else all cores)."""
     return default().num_threads()
+
+
+_ROT_DTYPES = {np.dtype(np.uint16): 0, np.dtype(np.float64): 2, np.dtype(np.float32): 3}
+
+
+def sign_bits(signs) -> np.ndarray:
+    """Pack a length-d sequence of +-1 into the uint32 bit mask the rotation
+    takes (bit i set = feature i is negated)."""
+    s = np.asarray(signs)
+    d = s.size
+    words = np.zeros((d + 31) // 32, dtype=np.uint32)
+    for i in np.nonzero(s < 0)[0]:
+        words[i >> 5] |= np.uint32(1) << np.uint32(i & 31)
+    return words
+
+
+def _rotate(lib, x, signs, rotate):
+    """y = x D H / sqrt(d) row by row (x: [..., d] as uint16 bfloat16 bits,
+    float32 or float64), in float64; ``signs`` is a length-d +-1 sequence."""
+    x = np.ascontiguousarray(x)
+    if x.dtype not in _ROT_DTYPES:
+        raise TypeError(f"rotate: unsupported dtype {x.dtype}")
+    d = x.shape[-1]
+    rows = x.size // d if d else 0
+    y = np.empty(x.shape, dtype=np.float64)
+    bits = None
+    if signs is not None:
+        bits = np.ascontiguousarray(sign_bits(signs))
+        if len(signs) != d:
+            raise ValueError("signs must have one entry per feature")
+    rc = lib.oracle_rotate(x.ctypes.data, _ROT_DTYPES[x.dtype], rows, d,
+                           bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)) if bits is not None else None,
+                           int(bool(rotate)), _dptr(y))
+    if rc != 0:
+        raise ValueError("oracle_rotate rejected its arguments (d must be a power of two)")
+    return y
+
+
+def _quantize(lib, y):
+    """Per-tensor E4M3 quantisation: (codes uint8 like y, scale s = amax / 448)."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    codes = np.empty(y.shape, dtype=np.uint8)
+    s = ctypes.c_double()
+    lib.oracle_quantize_e4m3(_dptr(y), y.size, ctypes.byref(s),
+                             codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    return codes, s.value
+
+
+def rotate(x, *, signs=None, rotate: bool = True) -> np.ndarray:
+    """Rotate every row of x by M = D H / sqrt(d) in float64 (identity when rotate=False)."""
+    return default().rotate(x, signs=signs, rotate=rotate)
+
+
+def quantize_e4m3(y) -> tuple:
+    """Per-tensor OCP E4M3 quantisation of float64 values: (codes, scale)."""
+    return default().quantize_e4m3(y)
+
+
+def e4m3_encode(v: float) -> int:
+    """The oracle's E4M3 encoder (nearest, ties to even, saturating at 448)."""
+    return default().e4m3_encode(v)
+
+
+def hadamard_entry(i: int, j: int) -> float:
+    """Sylvester-Hadamard entry H[i][j] = (-1)^popcount(i & j)."""
+    return default().hadamard_entry(i, j)

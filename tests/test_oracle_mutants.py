@@ -76,3 +76,51 @@ def test_unmutated_source_passes_every_pin():
     orc = oracle.default()
     for pin in PINS:
         pin(orc)
+
+
+# ---------------------------------------------------------------- rotation oracle
+from oracle.oracle import _ROT_SRC  # noqa: E402
+from rotate_pins import RPINS  # noqa: E402
+
+ROT_MUTANTS = {
+    "hadamard_sign_inverted": ("return (popcount64((uint64_t)(i & j)) & 1) ? -1.0 : 1.0;",
+                               "return (popcount64((uint64_t)(i & j)) & 1) ? 1.0 : -1.0;"),
+    "hadamard_or_instead_of_and": ("return (popcount64((uint64_t)(i & j)) & 1) ? -1.0 : 1.0;",
+                                   "return (popcount64((uint64_t)(i | j)) & 1) ? -1.0 : 1.0;"),
+    "normalisation_dropped": ("out[j] = acc * norm;", "out[j] = acc;"),
+    "signs_ignored": ("if (sign_bits && ((sign_bits[i >> 5] >> (i & 31)) & 1)) xi = -xi;", ""),
+    "transposed_product": ("acc += xi * oracle_hadamard_entry(i, j);",
+                           "acc += ro_load(x, dtype, r * d + j) * oracle_hadamard_entry(i, j);"),
+    "ties_to_odd": ("else c = (lo & 1) ? hi : lo;   /* tie: the even code */",
+                    "else c = (lo & 1) ? lo : hi;"),
+    "ties_round_up": ("else c = (lo & 1) ? hi : lo;   /* tie: the even code */", "else c = hi;"),
+    "no_saturation": ("if (a >= 448.0) return sign | 126;", "if (a >= 480.0) return sign | 127;"),
+    "subnormal_scale_wrong": ("return e == 0 ? ldexp((double)m / 8.0, -6)", "return e == 0 ? ldexp((double)m / 8.0, -7)"),
+    "scale_uses_240": ("const double s = amax > 0.0 ? amax / 448.0 : 1.0;",
+                       "const double s = amax > 0.0 ? amax / 240.0 : 1.0;"),
+    "amax_not_absolute": ("double a = fabs(y[k]);", "double a = y[k];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROT_MUTANTS))
+def test_rotation_mutant_is_caught(name, tmp_path):
+    old, new = ROT_MUTANTS[name]
+    src = open(_ROT_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / f"rmut_{name}.c"
+    path.write_text(src.replace(old, new))
+    lib_path = build(force=True, rot_src=str(path), out=str(tmp_path / f"librmut_{name}.so"))
+    mut = OracleLib(lib_path)
+    failures = []
+    for pin in RPINS:
+        try:
+            pin(mut)
+        except (AssertionError, ValueError, FloatingPointError):
+            failures.append(pin.__name__)
+    assert failures, f"rotation mutant {name} passed every pin"
+
+
+def test_unmutated_rotation_source_passes_every_pin():
+    orc = oracle.default()
+    for pin in RPINS:
+        pin(orc)
