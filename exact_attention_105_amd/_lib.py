@@ -1,8 +1,8 @@
 """ctypes binding of libfa.so (the C ABI declared in include/fa.h).
 
-Argument marshalling only: every step of the attention computation runs in
-the HIP kernels behind ``fa_fwd``.  There is no CPU fallback: if the library
-is missing or a call fails, this module raises.
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind ``fa_fwd`` and ``fa_rotate_quantize_e4m3``.  There is no CPU
+fallback: if the library is missing or a call fails, this module raises.
 """
 from __future__ import annotations
 
@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP8_E4M3 = 1
+FA_DTYPE_F32 = 2
 
 FA_SUCCESS = 0
 FA_ERROR_INVALID_VALUE = 1
@@ -21,7 +22,8 @@ FA_ERROR_NOT_SUPPORTED = 2
 FA_ERROR_LAUNCH_FAILURE = 3
 
 # every symbol include/fa.h declares
-EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_status_string", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_rotate_quantize_e4m3", "fa_rotate_quantize_validate",
+            "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -47,6 +49,11 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, fp, vp]
     lib.fa_fwd_validate.restype = i32
     lib.fa_fwd_validate.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, fp]
+    i64, up = ctypes.c_longlong, ctypes.POINTER(ctypes.c_uint)
+    lib.fa_rotate_quantize_e4m3.restype = i32
+    lib.fa_rotate_quantize_e4m3.argtypes = [vp, i32, i64, i32, i32, up, vp, vp, vp, vp]
+    lib.fa_rotate_quantize_validate.restype = i32
+    lib.fa_rotate_quantize_validate.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i32]
     lib.fa_version.restype = i32
@@ -80,6 +87,28 @@ def fa_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, 
     ds = _descale_arg(descale)
     return load().fa_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d,
                                   int(causal), float(scale), int(dtype), ds[0] if ds else None)
+
+
+def _sign_bits_arg(sign_bits):
+    if sign_bits is None:
+        return None, None
+    arr = (ctypes.c_uint * len(sign_bits))(*[int(w) for w in sign_bits])
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint)), arr
+
+
+def fa_rotate_quantize_e4m3(x_ptr, x_dtype, rows, d, rotate, sign_bits, codes_ptr, scale_ptr,
+                            work_ptr, stream) -> int:
+    """Raw call of fa_rotate_quantize_e4m3; ``sign_bits`` is a sequence of
+    d/32 words (host) or None.  Returns the status code."""
+    bits, keep = _sign_bits_arg(sign_bits)
+    return load().fa_rotate_quantize_e4m3(x_ptr, int(x_dtype), int(rows), int(d), int(rotate), bits,
+                                          codes_ptr, scale_ptr, work_ptr, stream)
+
+
+def fa_rotate_quantize_validate(x_ptr, x_dtype, rows, d, rotate, codes_ptr, scale_ptr, work_ptr) -> int:
+    """Raw call of fa_rotate_quantize_validate (pure host function)."""
+    return load().fa_rotate_quantize_validate(x_ptr, int(x_dtype), int(rows), int(d), int(rotate),
+                                              codes_ptr, scale_ptr, work_ptr)
 
 
 def version() -> int:

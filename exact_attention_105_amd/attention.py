@@ -67,3 +67,56 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     if st != _lib.FA_SUCCESS:
         raise _lib.FaError(st, _lib.status_string(st))
     return out, lse
+
+
+def sign_bits(signs) -> list:
+    """Pack a length-d sequence of +-1 (or booleans, True = negate) into the
+    d/32 words fa_rotate_quantize_e4m3 takes."""
+    words = [0] * ((len(signs) + 31) // 32)
+    for j, sgn in enumerate(signs):
+        neg = bool(sgn) if isinstance(sgn, (bool,)) else float(sgn) < 0
+        if neg:
+            words[j >> 5] |= 1 << (j & 31)
+    return words
+
+
+def rotate_quantize(x: torch.Tensor, *, rotate: bool = True, signs=None,
+                    codes: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                    work: torch.Tensor | None = None):
+    """Incoherent processing before FP8 attention: returns (codes, scale).
+
+    x: contiguous bfloat16 or float32 GPU tensor whose last dimension d is 64
+    or 128.  Every row is multiplied by M = D H / sqrt(d) (D = diag(signs),
+    H Sylvester-Hadamard; skipped when ``rotate`` is False) and the result is
+    quantised per tensor to E4M3: codes (torch.float8_e4m3fn, x's shape) and
+    a one-element float32 tensor s = max|x M| / 448.  Rotate Q and K with the
+    same ``signs`` (a length-d sequence of +-1); quantise V without rotation.
+    Runs on torch's current stream; ``work`` is a one-float workspace.
+    """
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    if x.dtype == torch.bfloat16:
+        xd = _lib.FA_DTYPE_BF16
+    elif x.dtype == torch.float32:
+        xd = _lib.FA_DTYPE_F32
+    else:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    d = x.shape[-1] if x.dim() else 0
+    rows = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    elif codes.shape != x.shape or codes.dtype not in _FP8_TYPES or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous float8_e4m3fn/uint8 tensor shaped like x")
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if work is None:
+        work = torch.empty(1, dtype=torch.float32, device=x.device)
+    if signs is not None and len(signs) != d:
+        raise ValueError("signs must have one entry per feature")
+    bits = sign_bits(signs) if signs is not None else None
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = _lib.fa_rotate_quantize_e4m3(x.data_ptr(), xd, rows, d, int(bool(rotate)), bits,
+                                      codes.data_ptr(), scale.data_ptr(), work.data_ptr(), stream)
+    if st != _lib.FA_SUCCESS:
+        raise _lib.FaError(st, _lib.status_string(st))
+    return codes, scale

@@ -23,8 +23,9 @@ extern "C" fa_status_t fa_fwd_validate(const void* q, const void* k, const void*
     if (Hq % Hkv != 0) return FA_ERROR_INVALID_VALUE;
     if (causal != 0 && causal != 1) return FA_ERROR_INVALID_VALUE;
     if (!isfinite(scale)) return FA_ERROR_INVALID_VALUE;
-    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3) return FA_ERROR_INVALID_VALUE;
-    if (dtype == FA_DTYPE_BF16 && descale_qkv != nullptr) return FA_ERROR_INVALID_VALUE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3 && dtype != FA_DTYPE_F32)
+        return FA_ERROR_INVALID_VALUE;
+    if (dtype != FA_DTYPE_FP8_E4M3 && descale_qkv != nullptr) return FA_ERROR_INVALID_VALUE;
     if (dtype == FA_DTYPE_FP8_E4M3) {
         if (descale_qkv == nullptr) return FA_ERROR_INVALID_VALUE;
         for (int i = 0; i < 3; ++i)
@@ -45,6 +46,7 @@ extern "C" fa_status_t fa_fwd_validate(const void* q, const void* k, const void*
     }
     if (dtype == FA_DTYPE_BF16 && d != 64 && d != 128) return FA_ERROR_NOT_SUPPORTED;
     if (dtype == FA_DTYPE_FP8_E4M3 && d != 128) return FA_ERROR_NOT_SUPPORTED;
+    if (dtype == FA_DTYPE_F32) return FA_ERROR_NOT_SUPPORTED;   // no fp32 attention kernel
     return FA_SUCCESS;
 }
 
@@ -97,6 +99,44 @@ extern "C" fa_status_t fa_fwd(const void* q, const void* k, const void* v, void*
                                              : fa::launch_fwd_bf16(p, d, causal != 0, stream);
     else
         err = fa::launch_fwd_fp8(p, d, causal != 0, stream);
+    return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
+}
+
+extern "C" fa_status_t fa_rotate_quantize_validate(const void* x, fa_dtype_t x_dtype, long long rows,
+                                                   int d, int rotate, const unsigned char* codes,
+                                                   const float* scale, const float* work) {
+    if (rows < 0 || d < 1) return FA_ERROR_INVALID_VALUE;
+    if (rotate != 0 && rotate != 1) return FA_ERROR_INVALID_VALUE;
+    if (x_dtype != FA_DTYPE_BF16 && x_dtype != FA_DTYPE_FP8_E4M3 && x_dtype != FA_DTYPE_F32)
+        return FA_ERROR_INVALID_VALUE;
+    if ((int64_t)rows * d > kMaxElems) return FA_ERROR_INVALID_VALUE;
+    if (scale == nullptr || work == nullptr || !aligned(scale, 4) || !aligned(work, 4))
+        return FA_ERROR_INVALID_VALUE;
+    if (rows > 0) {
+        if (x == nullptr || codes == nullptr) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(x, 8) || !aligned(codes, 2)) return FA_ERROR_INVALID_VALUE;
+    }
+    if (d != 64 && d != 128) return FA_ERROR_NOT_SUPPORTED;
+    if (x_dtype == FA_DTYPE_FP8_E4M3) return FA_ERROR_NOT_SUPPORTED;
+    return FA_SUCCESS;
+}
+
+extern "C" fa_status_t fa_rotate_quantize_e4m3(const void* x, fa_dtype_t x_dtype, long long rows, int d,
+                                               int rotate, const unsigned int* sign_bits,
+                                               unsigned char* codes, float* scale, float* work,
+                                               hipStream_t stream) {
+    const fa_status_t st = fa_rotate_quantize_validate(x, x_dtype, rows, d, rotate, codes, scale, work);
+    if (st != FA_SUCCESS) return st;
+    fa::RotParams p{};
+    p.x = x;
+    p.codes = codes;
+    p.scale = scale;
+    p.work = reinterpret_cast<unsigned*>(work);
+    p.rows = rows;
+    p.rotate = rotate;
+    if (rotate && sign_bits != nullptr)
+        for (int w = 0; w < d / 32; ++w) p.sign_bits[w] = sign_bits[w];
+    const hipError_t err = fa::launch_rotate_quantize(p, x_dtype == FA_DTYPE_F32, d, stream);
     return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
 }
 

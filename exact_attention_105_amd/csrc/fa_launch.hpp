@@ -18,4 +18,16 @@ hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t st
 bool decode_applies(const FwdParams& p, int d, bool is_bf16);
 hipError_t launch_fwd_decode(const FwdParams& p, bool causal, hipStream_t stream);
 
+// Random-sign Hadamard rotation + per-tensor E4M3 quantisation of [rows, d].
+struct RotParams {
+    const void* x;            // [rows, d] bf16 or fp32
+    uint8_t* codes;           // [rows, d] E4M3 codes (written)
+    float* scale;             // one float: amax / 448 (written)
+    unsigned* work;           // one word of workspace (amax bit pattern)
+    int64_t rows;
+    uint32_t sign_bits[4];    // bit j set: feature j is negated before the transform
+    int rotate;               // 0: quantise without rotating
+};
+hipError_t launch_rotate_quantize(const RotParams& p, bool x_is_f32, int d, hipStream_t stream);
+
 }  // namespace fa

@@ -35,10 +35,13 @@
 extern "C" {
 #endif
 
-/* Element type of Q, K and V.  O is always bfloat16, LSE always float32. */
+/* Element type of Q, K and V (fa_fwd: BF16 or FP8_E4M3; O is always
+ * bfloat16, LSE always float32) and of the input of fa_rotate_quantize_e4m3
+ * (BF16 or F32). */
 typedef enum {
     FA_DTYPE_BF16 = 0,       /* bfloat16 (upper half of an IEEE binary32) */
-    FA_DTYPE_FP8_E4M3 = 1    /* OCP FP8 E4M3 (bias 7, max 448, no inf), per-tensor scales */
+    FA_DTYPE_FP8_E4M3 = 1,   /* OCP FP8 E4M3 (bias 7, max 448, no inf), per-tensor scales */
+    FA_DTYPE_F32 = 2         /* IEEE binary32 */
 } fa_dtype_t;
 
 typedef enum {
@@ -92,6 +95,50 @@ fa_status_t fa_fwd_validate(const void* q, const void* k, const void* v, const v
                             const float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                             int causal, float scale, fa_dtype_t dtype,
                             const float* descale_qkv);
+
+/*
+ * fa_rotate_quantize_e4m3 -- incoherent processing before FP8 attention,
+ * asynchronous on `stream`.
+ *
+ * Rotates every row of x by M = D H / sqrt(d) -- D = diag(sigma) with
+ * sigma_j = -1 where bit j of sign_bits is set (+1 otherwise), H the d x d
+ * Sylvester-Hadamard matrix, H[i][j] = (-1)^popcount(i & j) -- and quantises
+ * the rotated tensor per tensor to OCP E4M3: s = max |x M| / 448 (1 when the
+ * tensor is all zeros), codes = E4M3(x M / s), rounded to nearest even and
+ * clamped to +-448 (page "FlashAttention-3 (DE)", systems-analysis.ru,
+ * technical innovation 3: a random orthogonal transform of Q and K spreads
+ * outlier features before the FP8 quantisation, and Q K^T is unchanged
+ * because M is orthogonal).  Rotate Q and K with the same signs; V is
+ * quantised without rotation (rotate = 0).  The codes and s are then the
+ * q/k/v and descale arguments of fa_fwd with FA_DTYPE_FP8_E4M3.
+ *
+ * Pointers (device memory, owned by the caller):
+ *   x      [rows, d] elements of x_dtype (FA_DTYPE_BF16 or FA_DTYPE_F32),
+ *          row-major, aligned to 8 bytes
+ *   codes  [rows, d] E4M3 codes (written), aligned to 2 bytes
+ *   scale  one float (written): s
+ *   work   one float of workspace the call overwrites; calls that share it
+ *          must be ordered on one stream
+ * sign_bits: HOST pointer to d / 32 words (bit j of word j / 32 negates
+ *   feature j), read during the call; NULL means no sign flips.  Ignored
+ *   when rotate == 0.
+ * rows >= 0 with rows * d < 2^31; d in {64, 128}; rotate 0 or 1.
+ *
+ * Returns FA_SUCCESS after the kernels are enqueued (the scale is written
+ * even for rows == 0), FA_ERROR_INVALID_VALUE for a null or misaligned
+ * pointer or an out-of-range size, FA_ERROR_NOT_SUPPORTED for another d or
+ * input dtype; on any error nothing is launched and the outputs are
+ * untouched.  No device memory is allocated.
+ */
+fa_status_t fa_rotate_quantize_e4m3(const void* x, fa_dtype_t x_dtype, long long rows, int d,
+                                    int rotate, const unsigned int* sign_bits,
+                                    unsigned char* codes, float* scale, float* work,
+                                    hipStream_t stream);
+
+/* The argument checks of fa_rotate_quantize_e4m3 as a pure host function. */
+fa_status_t fa_rotate_quantize_validate(const void* x, fa_dtype_t x_dtype, long long rows, int d,
+                                        int rotate, const unsigned char* codes, const float* scale,
+                                        const float* work);
 
 /* A static, human-readable description of a status code. */
 const char* fa_status_string(fa_status_t status);

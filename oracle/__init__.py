@@ -11,5 +11,5 @@ Parity status: every function here is pinned by ``tests/test_oracle_pins.py``,
 cases, invariants, brute force, library cross-checks).  The GPU-versus-oracle tolerances themselves come
 from the project's stated acceptance bounds, not from the pages.
 """
-from .oracle import (OracleLib, attention, build, decode, default, e4m3_encode,  # noqa: F401
+from .oracle import (OracleLib, attention, build, decode, default, e4m3_encode, encode_scaled,  # noqa: F401
                      hadamard_entry, num_threads, probs_row, quantize_e4m3, rotate, sign_bits)

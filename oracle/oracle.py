@@ -73,6 +73,8 @@ class OracleLib:
                                       ctypes.c_int, dp]
         lib.oracle_quantize_e4m3.restype = None
         lib.oracle_quantize_e4m3.argtypes = [dp, i64, dp, ctypes.POINTER(ctypes.c_uint8)]
+        lib.oracle_encode_scaled.restype = None
+        lib.oracle_encode_scaled.argtypes = [dp, i64, ctypes.c_double, ctypes.POINTER(ctypes.c_uint8)]
         lib.oracle_e4m3_encode.restype = ctypes.c_uint8
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
         lib.oracle_hadamard_entry.restype = ctypes.c_double
@@ -98,6 +100,13 @@ class OracleLib:
 
     def quantize_e4m3(self, y):
         return _quantize(self.lib, y)
+
+    def encode_scaled(self, y, s):
+        y = np.ascontiguousarray(y, dtype=np.float64)
+        codes = np.empty(y.shape, dtype=np.uint8)
+        self.lib.oracle_encode_scaled(_dptr(y), y.size, float(s),
+                                      codes.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+        return codes
 
     def e4m3_encode(self, v):
         return int(self.lib.oracle_e4m3_encode(float(v)))
@@ -292,3 +301,8 @@ def e4m3_encode(v: float) -> int:
 def hadamard_entry(i: int, j: int) -> float:
     """Sylvester-Hadamard entry H[i][j] = (-1)^popcount(i & j)."""
     return default().hadamard_entry(i, j)
+
+
+def encode_scaled(y, s: float) -> np.ndarray:
+    """E4M3 codes of y / s (the encoding step of the per-tensor quantisation)."""
+    return default().encode_scaled(y, s)

@@ -97,9 +97,14 @@ uint8_t oracle_e4m3_encode(double v) {
     const uint8_t sign = signbit(v) ? 0x80 : 0x00;
     double a = fabs(v);
     if (a >= 448.0) return sign | 126;
-    /* find the two neighbouring magnitudes lo <= a < hi by a linear scan */
-    int lo = 0;
-    while (lo + 1 <= 126 && e4m3_mag(lo + 1) <= a) ++lo;
+    /* the largest code lo with magnitude <= a (binary search over 0..126,
+     * whose magnitudes increase with the code) */
+    int lo = 0, top = 126;
+    while (lo < top) {
+        const int mid = (lo + top + 1) / 2;
+        if (e4m3_mag(mid) <= a) lo = mid;
+        else top = mid - 1;
+    }
     if (e4m3_mag(lo) == a || lo == 126) return sign | (uint8_t)lo;
     const int hi = lo + 1;
     const double dlo = a - e4m3_mag(lo), dhi = e4m3_mag(hi) - a;
@@ -108,6 +113,13 @@ uint8_t oracle_e4m3_encode(double v) {
     else if (dhi < dlo) c = hi;
     else c = (lo & 1) ? hi : lo;   /* tie: the even code */
     return sign | (uint8_t)c;
+}
+
+/* codes[k] = E4M3(y[k] / s) for a given scale s (the encoding step of the
+ * per-tensor quantisation below, for a subset of a tensor). */
+void oracle_encode_scaled(const double* y, int64_t n, double s, uint8_t* codes) {
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < n; ++k) codes[k] = oracle_e4m3_encode(y[k] / s);
 }
 
 /*

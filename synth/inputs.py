@@ -166,16 +166,13 @@ def generate(cfg: Config, *, outlier_mult: float = 20.0):
                        outlier_mult=outlier_mult)
 
 
-def make_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed, *, outlier_mult: float = 20.0):
+def make_float_inputs(B, Hq, Hkv, Nq, Nk, d, seed, *, outlier_mult: float = 20.0):
+    """The float32 Q, K, V of the FP8 recipe before quantisation: normals with
+    the outlier channels multiplied by ``outlier_mult``."""
     rng = np.random.Generator(np.random.PCG64(seed))
     qf = normals(rng, (B, Hq, Nq, d))
     kf = normals(rng, (B, Hkv, Nk, d))
     vf = normals(rng, (B, Hkv, Nk, d))
-    if dtype == "bf16":
-        return {"q": f32_to_bf16_bits(qf), "k": f32_to_bf16_bits(kf),
-                "v": f32_to_bf16_bits(vf), "descale": None}
-    if dtype != "e4m3":
-        raise ValueError(f"unknown dtype {dtype}")
     # outlier channels are drawn over the key/value heads; a query head gets
     # the channels of the key/value head it reads (the same set when Hq == Hkv)
     ch = outlier_channels(seed, Hkv, d)
@@ -185,6 +182,20 @@ def make_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed, *, outlier_mult: float = 20.
         t[:, hs, :, ts] *= np.float32(outlier_mult)
     for gi in range(g):
         qf[:, hs * g + gi, :, ts] *= np.float32(outlier_mult)
+    return qf, kf, vf
+
+
+def make_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed, *, outlier_mult: float = 20.0):
+    if dtype == "bf16":
+        rng = np.random.Generator(np.random.PCG64(seed))
+        qf = normals(rng, (B, Hq, Nq, d))
+        kf = normals(rng, (B, Hkv, Nk, d))
+        vf = normals(rng, (B, Hkv, Nk, d))
+        return {"q": f32_to_bf16_bits(qf), "k": f32_to_bf16_bits(kf),
+                "v": f32_to_bf16_bits(vf), "descale": None}
+    if dtype != "e4m3":
+        raise ValueError(f"unknown dtype {dtype}")
+    qf, kf, vf = make_float_inputs(B, Hq, Hkv, Nq, Nk, d, seed, outlier_mult=outlier_mult)
     qc, sq = quantise_e4m3(qf)
     kc, sk = quantise_e4m3(kf)
     vc, sv = quantise_e4m3(vf)

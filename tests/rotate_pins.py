@@ -164,6 +164,8 @@ def rpin_quantize_scale_and_extremes(orc):
     assert np.all(np.abs(dec - y) <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10 * s) + 1e-12)
     # the quantiser's codes are the encoder's codes of y / s
     assert np.array_equal(codes.reshape(-1), np.array([orc.e4m3_encode(v / s) for v in y.reshape(-1)], dtype=np.uint8))
+    # the encoding step alone, with the same scale, gives the same codes
+    assert np.array_equal(orc.encode_scaled(y, s), codes)
     # the largest magnitude negative: the scale comes from |min|
     yn = y.copy()
     yn[0, 0] = -10 * amax

@@ -93,3 +93,40 @@ def test_invalid_arguments(lib, kw):
                                 dict(dtype=_lib.FA_DTYPE_FP8_E4M3, descale=(1.0, 1.0, 1.0), d=64)])
 def test_unsupported_combinations(lib, kw):
     assert validate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
+
+
+# ---------------------------------------------------------------- fa_rotate_quantize_e4m3
+RGOOD = dict(x=4096, x_dtype=_lib.FA_DTYPE_F32, rows=1000, d=128, rotate=1, codes=8192, scale=12288,
+             work=12292)
+
+
+def rvalidate(**kw):
+    a = dict(RGOOD)
+    a.update(kw)
+    return _lib.fa_rotate_quantize_validate(a["x"], a["x_dtype"], a["rows"], a["d"], a["rotate"],
+                                            a["codes"], a["scale"], a["work"])
+
+
+def test_rotate_valid_arguments(lib):
+    assert rvalidate() == _lib.FA_SUCCESS
+    assert rvalidate(x_dtype=_lib.FA_DTYPE_BF16, d=64, rotate=0) == _lib.FA_SUCCESS
+    assert rvalidate(rows=0, x=None, codes=None) == _lib.FA_SUCCESS    # scale still written
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rows=-1), dict(d=0), dict(rotate=2), dict(x_dtype=9), dict(scale=None), dict(work=None),
+    dict(x=None), dict(codes=None), dict(x=4096 + 4), dict(codes=8192 + 1), dict(scale=12288 + 2),
+    dict(rows=1 << 24, d=128),
+])
+def test_rotate_invalid_arguments(lib, kw):
+    assert rvalidate(**kw) == _lib.FA_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=256), dict(d=32), dict(x_dtype=_lib.FA_DTYPE_FP8_E4M3)])
+def test_rotate_unsupported(lib, kw):
+    assert rvalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
+
+
+def test_fwd_rejects_fp32_attention(lib):
+    assert validate(dtype=_lib.FA_DTYPE_F32) == _lib.FA_ERROR_NOT_SUPPORTED
+    assert validate(dtype=_lib.FA_DTYPE_F32, descale=(1.0, 1.0, 1.0)) == _lib.FA_ERROR_INVALID_VALUE
