@@ -151,6 +151,107 @@ def gemm_reference(args):
     del c
 
 
+ROTATE_SOURCES = ("fa_rotate.hip", "fa_device.hpp", "fa_launch.hpp")
+
+
+def rotate_source_hash() -> str:
+    """Hash of what the rotation kernels are compiled from."""
+    from exact_attention_105_amd import build as _build
+    csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ROTATE_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    h.update(" ".join(_build.HIPCC_FLAGS + _build.SOURCE_FLAGS.get(ROTATE_SOURCES[0], [])).encode())
+    return h.hexdigest()[:16]
+
+
+def rotate_cpu_baseline(xf, signs, budget_s: float):
+    """The oracle's rotation (dense fp64 product) and E4M3 encoding on sampled
+    rows for about budget_s seconds; returns (GB/s of the call's algorithmic
+    bytes, threads, sample description)."""
+    import oracle
+    rows_all = xf.shape[0]
+    rng = np.random.default_rng(2024)
+    d = xf.shape[1]
+
+    def run(n):
+        pick = np.sort(rng.choice(rows_all, size=n, replace=False))
+        t0 = time.perf_counter()
+        y = oracle.rotate(xf[pick], signs=signs)
+        oracle.quantize_e4m3(y)
+        return time.perf_counter() - t0
+
+    n = 256
+    while True:
+        dt = run(n)
+        if dt >= 0.1 * budget_s or n >= rows_all:
+            break
+        n = min(rows_all, n * 4)
+    n = int(min(rows_all, max(n, n * (budget_s / max(dt, 1e-9)))))
+    dt = run(n)
+    bytes_per_row = d * (xf.dtype.itemsize + 1)
+    return n * bytes_per_row / dt / 1e9, oracle.num_threads(), f"{n} of {rows_all} rows ({dt:.1f} s)"
+
+
+def rotate_bench(args):
+    """One fa_rotate_quantize_e4m3 call per step on the FP8 workload's query
+    tensor (B=4, H=16, N=8192, d=128, fp32 with outlier channels): rotation
+    by D H / sqrt(d) and per-tensor E4M3 quantisation.  HBM-bound:
+    algorithmic bytes = the fp32 input read once plus the codes written once
+    (the two-pass design reads the input twice)."""
+    import torch
+    from exact_attention_105_amd import load, rotate_quantize
+    from synth.inputs import CONFIGS, make_float_inputs
+    load()
+    cfg = CONFIGS["fp8"]
+    qf, _, _ = make_float_inputs(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk, cfg.d, cfg.seed)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(qf).to(dev)
+    signs = np.where(np.random.default_rng(cfg.seed + 7).random(cfg.d) < 0.5, -1.0, 1.0)
+    codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    work = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        rotate_quantize(x, signs=signs, codes=codes, scale=scale, work=work)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        rotate_quantize(x, signs=signs, codes=codes, scale=scale, work=work)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    n = x.numel()
+    alg = 4 * n + n
+    gbs = alg / (ms * 1e-3) / 1e9
+    traffic = None
+    path = os.path.join(ROOT, "profiles", "traffic_rotate_fp8_query.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == rotate_source_hash():
+            traffic = t.get("hbm_bytes_per_call")
+    cpu = None
+    if args.cpu_budget > 0:
+        v, threads, sample = rotate_cpu_baseline(qf.reshape(-1, cfg.d), signs, args.cpu_budget)
+        cpu = {"value": v, "unit": "GB/s", "cores": threads, "kind": "oracle", "sample": sample}
+    del qf
+    print(json.dumps({"metric": "rotate+quantize E4M3 GB/s (algorithmic) on 1 MI355X", "value": gbs,
+                      "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+                      "data": "synthetic",
+                      "config": {"workload": "fp8 query tensor rotate+quantize", "rows": n // cfg.d, "d": cfg.d,
+                                 "input": "f32", "algorithmic_bytes_per_call": alg,
+                                 "two_pass_hbm_bytes_per_call": 2 * 4 * n + n},
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
+                                   "scope": "one fa_rotate_quantize_e4m3 call (rot_clear, rot_amax, rot_quant)"},
+                      "cpu_baseline": cpu}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +262,8 @@ def main():
                     help="seconds of oracle work for the cpu_baseline leg (0 to skip)")
     ap.add_argument("--gemm-reference", type=int, default=0,
                     help="instead of attention, time a bf16 n x n x n torch.matmul (vendor GEMM context)")
+    ap.add_argument("--rotate", action="store_true",
+                    help="instead of attention, time the Hadamard rotation + E4M3 quantisation step")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
@@ -170,6 +273,9 @@ def main():
         return
     if args.gemm_reference > 0:
         gemm_reference(args)
+        return
+    if args.rotate:
+        rotate_bench(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",

@@ -114,7 +114,7 @@ extern "C" fa_status_t fa_rotate_quantize_validate(const void* x, fa_dtype_t x_d
         return FA_ERROR_INVALID_VALUE;
     if (rows > 0) {
         if (x == nullptr || codes == nullptr) return FA_ERROR_INVALID_VALUE;
-        if (!aligned(x, 8) || !aligned(codes, 2)) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(x, 16) || !aligned(codes, 16)) return FA_ERROR_INVALID_VALUE;
     }
     if (d != 64 && d != 128) return FA_ERROR_NOT_SUPPORTED;
     if (x_dtype == FA_DTYPE_FP8_E4M3) return FA_ERROR_NOT_SUPPORTED;

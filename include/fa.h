@@ -114,8 +114,8 @@ fa_status_t fa_fwd_validate(const void* q, const void* k, const void* v, const v
  *
  * Pointers (device memory, owned by the caller):
  *   x      [rows, d] elements of x_dtype (FA_DTYPE_BF16 or FA_DTYPE_F32),
- *          row-major, aligned to 8 bytes
- *   codes  [rows, d] E4M3 codes (written), aligned to 2 bytes
+ *          row-major, aligned to 16 bytes
+ *   codes  [rows, d] E4M3 codes (written), aligned to 16 bytes
  *   scale  one float (written): s
  *   work   one float of workspace the call overwrites; calls that share it
  *          must be ordered on one stream

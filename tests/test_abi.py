@@ -115,7 +115,8 @@ def test_rotate_valid_arguments(lib):
 
 @pytest.mark.parametrize("kw", [
     dict(rows=-1), dict(d=0), dict(rotate=2), dict(x_dtype=9), dict(scale=None), dict(work=None),
-    dict(x=None), dict(codes=None), dict(x=4096 + 4), dict(codes=8192 + 1), dict(scale=12288 + 2),
+    dict(x=None), dict(codes=None), dict(x=4096 + 4), dict(x=4096 + 8), dict(codes=8192 + 1),
+    dict(codes=8192 + 4), dict(codes=8192 + 8), dict(scale=12288 + 2),
     dict(rows=1 << 24, d=128),
 ])
 def test_rotate_invalid_arguments(lib, kw):

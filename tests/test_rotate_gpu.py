@@ -130,6 +130,26 @@ def test_full_size_fp8_query_tensor():
     check_codes(codes.reshape(-1, d)[rows], y[rows], s_ref, s, x_l1, "full-size Q, 4096 sampled rows")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_grid_stride_and_ragged_chunk(d):
+    """bf16 rows packed several to a 1 KiB chunk, more chunks than one pass of
+    the grid covers, and a last chunk that is only partly inside the tensor."""
+    rows = (1024 * 4 * 2) * (1024 // d) + 13
+    rng = np.random.default_rng(d + 31)
+    x = rng.standard_normal((rows, d)).astype(np.float32)
+    x[:, rng.integers(0, d, size=3)] *= 30.0
+    signs = random_signs(d, 5 * d)
+    say(f"rotate-quantize grid-stride rows={rows} d={d} bf16")
+    codes, s, host = run(x, "bf16", True, signs)
+    y = oracle.rotate(host, signs=signs)
+    s_ref = np.abs(y).max() / 448.0
+    assert abs(s / s_ref - 1.0) <= 1e-5, (s, s_ref)
+    pick = np.concatenate([np.arange(rows - 64, rows),
+                           np.random.default_rng(9).choice(rows - 64, size=4096, replace=False)])
+    x_l1 = np.abs(oracle.rotate(host[pick], rotate=False)).sum(axis=-1)
+    check_codes(codes[pick], y[pick], s_ref, s, x_l1, f"grid-stride d={d}: last 64 + 4096 sampled rows")
+
+
 def rrmse(o, ref):
     return float(np.linalg.norm(o - ref) / np.linalg.norm(ref))
 
