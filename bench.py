@@ -42,16 +42,27 @@ def kernel_source(cfg) -> str:
     return "fa_fwd_bf16.hip"
 
 
+def _code_only(text: bytes) -> bytes:
+    """Source text without comments and with whitespace collapsed, so that a
+    comment edit does not disown counters taken on unchanged code."""
+    import re
+    t = text.decode()
+    t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+    t = re.sub(r"//[^\n]*", " ", t)
+    return " ".join(t.split()).encode()
+
+
 def kernel_source_hash(cfg) -> str:
-    """Hash of what the workload's kernel is compiled from: its source file,
-    the shared device header and that file's extra compiler flags."""
+    """Hash of what the workload's kernel is compiled from: its source file
+    and the shared device header (code only, comments ignored) and that
+    file's extra compiler flags."""
     from exact_attention_105_amd import build as _build
     src = kernel_source(cfg)
     csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
     h = hashlib.sha256()
     for f in (src, "fa_device.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+            h.update(f.encode() + _code_only(fh.read()))
     h.update(" ".join(_build.HIPCC_FLAGS + _build.SOURCE_FLAGS.get(src, [])).encode())
     return h.hexdigest()[:16]
 
@@ -161,7 +172,7 @@ def rotate_source_hash() -> str:
     h = hashlib.sha256()
     for f in ROTATE_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+            h.update(f.encode() + _code_only(fh.read()))
     h.update(" ".join(_build.HIPCC_FLAGS + _build.SOURCE_FLAGS.get(ROTATE_SOURCES[0], [])).encode())
     return h.hexdigest()[:16]
 

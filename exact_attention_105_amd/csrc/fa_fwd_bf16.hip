@@ -19,11 +19,12 @@
 //                    transposing read ds_read_b64_tr_b16 (16 lanes read a
 //                    4-key x 16-d block; each lane receives one d column of
 //                    4 keys), B = P straight from the score registers.
-// Two workgroups (eight waves) share a CU, so one wave's softmax overlaps
-// the other's MFMAs on each SIMD.  Short 32-key tiles make the waves
-// alternate between MFMA and VALU phases often, which measured faster than
-// 64-key tiles at the same occupancy (FA_BF16_BN); deeper LDS pipelines
-// (FA_BF16_NSTAGE) and more workgroups per CU (FA_BF16_OCC) did not help.
+// Three workgroups (twelve waves) share a CU at d = 128 (FA_BF16_OCC), so
+// one wave's softmax overlaps the others' MFMAs on each SIMD; the MFMA
+// blocks run at raised wave priority so that a wave reaching its matrix work
+// issues it first.  Short 32-key tiles make the waves alternate between MFMA
+// and VALU phases often, which measured faster than 64-key tiles at the same
+// occupancy (FA_BF16_BN); deeper LDS pipelines (FA_BF16_NSTAGE) did not help.
 // 64 rows per wave (FA_BF16_RW128 / FA_BF16_RW64 = 64) would feed every K
 // and V^T fragment read from LDS to two MFMAs, but needs the accumulators in
 // AGPRs and runs one workgroup per CU; measured slower.

@@ -3,7 +3,7 @@
 // Low-precision attention (page "FlashAttention-3 (DE)", systems-analysis.ru,
 // section on low precision: FP8 doubles the matrix throughput at the cost of
 // dynamic range).  The structure follows the bf16 kernel (fa_fwd_bf16.hip):
-// BM = 128 query rows per workgroup (32 per wave, two workgroups per CU),
+// BM = 128 query rows per workgroup (32 per wave, up to three workgroups per CU),
 // 64-key K/V tiles copied straight into double-buffered LDS, the query index
 // on the MFMA column side so each lane owns one query row, and the online
 // softmax with a lazily moved reference in registers.  Differences:
