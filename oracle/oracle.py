@@ -15,7 +15,9 @@ query rows).  This wrapper only marshals numpy arrays into that library:
 * ``decode``      -- the oracle's own bfloat16 / OCP-E4M3 decoders;
 * ``rotate``, ``quantize_e4m3``, ``e4m3_encode`` -- the random-sign Hadamard
   rotation and per-tensor FP8 quantisation of page "FlashAttention-3 (DE)",
-  systems-analysis.ru, technical innovation 3 (``rotate_oracle.c``).
+  systems-analysis.ru, technical innovation 3 (``rotate_oracle.c``);
+* ``attention_bwd``, ``bwd_dq_rows`` -- the gradients dQ, dK, dV of
+  attention by the chain rule through the definition (``attn_bwd_oracle.c``).
 
 Inputs are the exact bytes the GPU receives: ``uint16`` arrays holding
 bfloat16 bit patterns, ``uint8`` arrays holding E4M3 codes (plus per-tensor
@@ -32,6 +34,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
 _ROT_SRC = os.path.join(_HERE, "rotate_oracle.c")
+_BWD_SRC = os.path.join(_HERE, "attn_bwd_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 DTYPES = {"bf16": 0, "e4m3": 1, "f64": 2}
@@ -40,12 +43,13 @@ _NP = {"bf16": np.uint16, "e4m3": np.uint8, "f64": np.float64}
 _default = None
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH, rot_src: str = _ROT_SRC) -> str:
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH, rot_src: str = _ROT_SRC,
+          bwd_src: str = _BWD_SRC) -> str:
     """Compile the oracle C sources into a shared library with gcc (IEEE semantics)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-fno-fast-math", "-ffp-contract=off", src, rot_src, "-o", tmp, "-lm"]
+               "-fno-fast-math", "-ffp-contract=off", src, rot_src, bwd_src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out
@@ -79,6 +83,12 @@ class OracleLib:
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
         lib.oracle_hadamard_entry.restype = ctypes.c_double
         lib.oracle_hadamard_entry.argtypes = [i64, i64]
+        lib.oracle_attention_bwd.restype = ctypes.c_int
+        lib.oracle_attention_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                             ctypes.c_int, ctypes.c_double, dp, dp, dp]
+        lib.oracle_bwd_dq_rows.restype = ctypes.c_int
+        lib.oracle_bwd_dq_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64,
+                                           ctypes.c_int, ctypes.c_double, ctypes.POINTER(i64), i64, dp]
         self.lib = lib
         self.path = path
 
@@ -91,6 +101,12 @@ class OracleLib:
 
     def decode(self, codes, dtype, descale=1.0):
         return _decode(self.lib, codes, dtype, descale)
+
+    def attention_bwd(self, q, k, v, dout, *, causal, scale, dtype="bf16"):
+        return _attention_bwd(self.lib, q, k, v, dout, causal, scale, dtype)
+
+    def bwd_dq_rows(self, q, k, v, dout, *, causal, scale, rows, dtype="bf16"):
+        return _bwd_dq_rows(self.lib, q, k, v, dout, causal, scale, rows, dtype)
 
     def num_threads(self):
         return int(self.lib.oracle_num_threads())
@@ -119,7 +135,7 @@ def default() -> OracleLib:
     """The oracle built from its C sources (rebuilt when a source is newer)."""
     global _default
     if _default is None:
-        newest = max(os.path.getmtime(_SRC), os.path.getmtime(_ROT_SRC))
+        newest = max(os.path.getmtime(_SRC), os.path.getmtime(_ROT_SRC), os.path.getmtime(_BWD_SRC))
         if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
             build(force=True)
         _default = OracleLib(_LIB_PATH)
@@ -196,6 +212,44 @@ def _probs_row(lib, q, k, v, causal, scale, row, dtype, descale):
     if rc < 0:
         raise ValueError("oracle_probs_row rejected its arguments")
     return p[:Nk]
+
+
+def _prep_bwd(q, k, v, dout, dtype):
+    if dtype not in ("bf16", "f64"):
+        raise ValueError("the backward oracle takes bf16 or f64 inputs")
+    q, k, v, dims = _prep(q, k, v, dtype)
+    dout = np.ascontiguousarray(dout)
+    if dout.dtype != q.dtype or dout.shape != q.shape:
+        raise ValueError(f"dout must match q: {dout.dtype}{dout.shape} vs {q.dtype}{q.shape}")
+    return q, k, v, dout, dims
+
+
+def _attention_bwd(lib, q, k, v, dout, causal, scale, dtype):
+    """Return (dQ, dK, dV) in float64, shaped like q, k, v."""
+    q, k, v, dout, (B, Hq, Hkv, Nq, Nk, d) = _prep_bwd(q, k, v, dout, dtype)
+    dq = np.zeros((B, Hq, Nq, d), dtype=np.float64)
+    dk = np.zeros((B, Hkv, Nk, d), dtype=np.float64)
+    dv = np.zeros((B, Hkv, Nk, d), dtype=np.float64)
+    rc = lib.oracle_attention_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                  DTYPES[dtype], B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                                  _dptr(dq), _dptr(dk), _dptr(dv))
+    if rc != 0:
+        raise ValueError("oracle_attention_bwd rejected its arguments")
+    return dq, dk, dv
+
+
+def _bwd_dq_rows(lib, q, k, v, dout, causal, scale, rows, dtype):
+    """dQ of the listed rows (flat (b*Hq + h)*Nq + i), [n, d] float64."""
+    q, k, v, dout, (B, Hq, Hkv, Nq, Nk, d) = _prep_bwd(q, k, v, dout, dtype)
+    rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.zeros((max(rows_arr.size, 1), d), dtype=np.float64)
+    rc = lib.oracle_bwd_dq_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                DTYPES[dtype], B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale),
+                                rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows_arr.size,
+                                _dptr(out))
+    if rc != 0:
+        raise ValueError("oracle_bwd_dq_rows rejected its arguments")
+    return out[:rows_arr.size]
 
 
 def _decode(lib, codes, dtype, descale):
@@ -306,3 +360,13 @@ def hadamard_entry(i: int, j: int) -> float:
 def encode_scaled(y, s: float) -> np.ndarray:
     """E4M3 codes of y / s (the encoding step of the per-tensor quantisation)."""
     return default().encode_scaled(y, s)
+
+
+def attention_bwd(q, k, v, dout, *, causal: bool, scale: float, dtype: str = "bf16"):
+    """Gradients (dQ, dK, dV) of attention for upstream gradient dout, float64."""
+    return default().attention_bwd(q, k, v, dout, causal=causal, scale=scale, dtype=dtype)
+
+
+def bwd_dq_rows(q, k, v, dout, *, causal: bool, scale: float, rows, dtype: str = "bf16"):
+    """dQ of the listed rows (flat (b*Hq + h)*Nq + i) only, [n, d] float64."""
+    return default().bwd_dq_rows(q, k, v, dout, causal=causal, scale=scale, rows=rows, dtype=dtype)

@@ -124,3 +124,61 @@ def test_unmutated_rotation_source_passes_every_pin():
     orc = oracle.default()
     for pin in RPINS:
         pin(orc)
+
+
+# ---------------------------------------------------------------- backward oracle
+from oracle.oracle import _BWD_SRC  # noqa: E402
+from bwd_pins import BPINS  # noqa: E402
+
+BWD_MUTANTS = {
+    "jacobian_row_term_dropped": ("r->dprow[j] = r->prow[j] * (r->dprow[j] - Dsum);",
+                                  "r->dprow[j] = r->prow[j] * r->dprow[j];"),
+    "jacobian_sign_flipped": ("r->dprow[j] = r->prow[j] * (r->dprow[j] - Dsum);",
+                              "r->dprow[j] = r->prow[j] * (Dsum - r->dprow[j]);"),
+    "row_term_unweighted": ("Dsum += r->prow[j] * r->dprow[j];", "Dsum += r->dprow[j];"),
+    "dq_scale_dropped": ("dqi[t] += scale * ds * bw_load(k, dtype, koff + t);",
+                         "dqi[t] += ds * bw_load(k, dtype, koff + t);"),
+    "dk_scale_squared": ("dk[koff + t] += scale * ds * r.qrow[t];",
+                         "dk[koff + t] += scale * scale * ds * r.qrow[t];"),
+    "dk_uses_do": ("dk[koff + t] += scale * ds * r.qrow[t];", "dk[koff + t] += scale * ds * r.dorow[t];"),
+    "dv_uses_ds": ("dv[koff + t] += pj * r.dorow[t];", "dv[koff + t] += ds * r.dorow[t];"),
+    "dv_uses_q": ("dv[koff + t] += pj * r.dorow[t];", "dv[koff + t] += pj * r.qrow[t];"),
+    "dp_uses_k": ("for (int64_t t = 0; t < d; ++t) dot += r->dorow[t] * bw_load(p->v, p->dtype, voff + t);",
+                  "for (int64_t t = 0; t < d; ++t) dot += r->dorow[t] * bw_load(p->k, p->dtype, voff + t);"),
+    "softmax_not_normalised": ("for (int64_t j = 0; j < Nk; ++j) r->prow[j] /= L;", ""),
+    "causal_off_by_one": ("if (p->causal && j > i + (Nk - p->Nq))", "if (p->causal && j >= i + (Nk - p->Nq))"),
+    "causal_top_left": ("if (p->causal && j > i + (Nk - p->Nq))", "if (p->causal && j > i)"),
+    "gqa_interleaved": ("    const int64_t kvh = h / (p->Hq / p->Hkv);", "    const int64_t kvh = h % p->Hkv;"),
+    "key_row_reversed": ("const int64_t koff = ((b * Hkv + kvh) * Nk + j) * d;\n                            for",
+                         "const int64_t koff = ((b * Hkv + kvh) * Nk + (Nk - 1 - j)) * d;\n                            for"),
+    "scale_missing_in_scores": ("r->prow[j] = p->scale * dot;", "r->prow[j] = dot;"),
+    "rows_dq_uses_v": ("out[t] += scale * r.dprow[j] * bw_load(k, dtype, koff + t);",
+                       "out[t] += scale * r.dprow[j] * bw_load(v, dtype, koff + t);"),
+    "bf16_shift_wrong": ("uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;",
+                         "uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 15;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name, tmp_path):
+    old, new = BWD_MUTANTS[name]
+    src = open(_BWD_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = tmp_path / f"bmut_{name}.c"
+    path.write_text(src.replace(old, new))
+    lib_path = build(force=True, bwd_src=str(path), out=str(tmp_path / f"libbmut_{name}.so"))
+    mut = OracleLib(lib_path)
+    failures = []
+    for pin in BPINS:
+        try:
+            pin(mut)
+        except (AssertionError, ValueError, FloatingPointError):
+            failures.append(pin.__name__)
+    assert failures, f"backward mutant {name} passed every pin"
+
+
+def test_unmutated_backward_source_passes_every_pin():
+    orc = oracle.default()
+    for pin in BPINS:
+        pin(orc)
+
