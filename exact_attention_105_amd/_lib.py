@@ -1,7 +1,7 @@
 """ctypes binding of libfa.so (the C ABI declared in include/fa.h).
 
 Argument marshalling only: every step of the computation runs in the HIP
-kernels behind ``fa_fwd`` and ``fa_rotate_quantize_e4m3``.  There is no CPU
+kernels behind ``fa_fwd``, ``fa_bwd`` and ``fa_rotate_quantize_e4m3``.  There is no CPU
 fallback: if the library is missing or a call fails, this module raises.
 """
 from __future__ import annotations
@@ -22,8 +22,8 @@ FA_ERROR_NOT_SUPPORTED = 2
 FA_ERROR_LAUNCH_FAILURE = 3
 
 # every symbol include/fa.h declares
-EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_rotate_quantize_e4m3", "fa_rotate_quantize_validate",
-            "fa_status_string", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_bwd", "fa_bwd_validate", "fa_rotate_quantize_e4m3",
+            "fa_rotate_quantize_validate", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -54,6 +54,10 @@ def load(path: str = LIB_PATH):
     lib.fa_rotate_quantize_e4m3.argtypes = [vp, i32, i64, i32, i32, up, vp, vp, vp, vp]
     lib.fa_rotate_quantize_validate.restype = i32
     lib.fa_rotate_quantize_validate.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd.argtypes = [vp] * 10 + [i32] * 7 + [f32, i32, vp]
+    lib.fa_bwd_validate.restype = i32
+    lib.fa_bwd_validate.argtypes = [vp] * 10 + [i32] * 7 + [f32, i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i32]
     lib.fa_version.restype = i32
@@ -87,6 +91,20 @@ def fa_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, 
     ds = _descale_arg(descale)
     return load().fa_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d,
                                   int(causal), float(scale), int(dtype), ds[0] if ds else None)
+
+
+def fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr, B, Hq, Hkv, Nq,
+           Nk, d, causal, scale, dtype, stream) -> int:
+    """Raw call of fa_bwd with integer device pointers; returns the status code."""
+    return load().fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr, B, Hq,
+                         Hkv, Nq, Nk, d, int(causal), float(scale), int(dtype), stream)
+
+
+def fa_bwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr, B, Hq, Hkv,
+                    Nq, Nk, d, causal, scale, dtype) -> int:
+    """Raw call of fa_bwd_validate (pure host function); returns the status code."""
+    return load().fa_bwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr,
+                                  B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale), int(dtype))
 
 
 def _sign_bits_arg(sign_bits):

@@ -1,7 +1,8 @@
-"""PyTorch-facing wrapper of the attention forward pass.
+"""PyTorch-facing wrappers of the attention library.
 
 PyTorch provides device memory and the current HIP stream; the computation
-is entirely the HIP library's (``fa_fwd`` in include/fa.h).
+is entirely the HIP library's (``fa_fwd``, ``fa_bwd`` and
+``fa_rotate_quantize_e4m3`` in include/fa.h).
 """
 from __future__ import annotations
 
@@ -67,6 +68,52 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     if st != _lib.FA_SUCCESS:
         raise _lib.FaError(st, _lib.status_string(st))
     return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, *, causal: bool = False, scale: float | None = None,
+        dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+        workspace: torch.Tensor | None = None):
+    """Exact attention backward: returns (dQ, dK, dV), bfloat16.
+
+    q, k, v, ``causal`` and ``scale`` as given to ``fwd``; o and lse are the
+    outputs ``fwd`` returned for them, dout the gradient of the loss with
+    respect to o (bfloat16, o's shape).  ``workspace`` holds 2*B*Hq*Nq
+    floats.  Runs on torch's current stream.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 [B, H, N, d] GPU tensor")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk_ = k.shape
+    if Bk != B or dk_ != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    def out_like(t, ref, name):
+        if t is None:
+            return torch.empty(ref.shape, dtype=torch.bfloat16, device=ref.device)
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(ref.shape) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor shaped like {tuple(ref.shape)}")
+        return t
+
+    dq, dk, dv = out_like(dq, q, "dq"), out_like(dk, k, "dk"), out_like(dv, v, "dv")
+    if workspace is None:
+        workspace = torch.empty(max(2 * B * Hq * Nq, 1), dtype=torch.float32, device=q.device)
+    elif workspace.dtype != torch.float32 or workspace.numel() < 2 * B * Hq * Nq:
+        raise ValueError("workspace must hold 2*B*Hq*Nq float32 values")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                     B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale, _lib.FA_DTYPE_BF16, stream)
+    if st != _lib.FA_SUCCESS:
+        raise _lib.FaError(st, _lib.status_string(st))
+    return dq, dk, dv
 
 
 def sign_bits(signs) -> list:

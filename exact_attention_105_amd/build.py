@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_fwd_decode.hip", "fa_rotate.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_fwd_decode.hip", "fa_rotate.hip", "fa_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_bwd.hpp"
 #include "fa_launch.hpp"
 
 namespace {
@@ -151,3 +152,68 @@ extern "C" const char* fa_status_string(fa_status_t status) {
 }
 
 extern "C" int fa_version(void) { return 100; }
+
+extern "C" fa_status_t fa_bwd_validate(const void* q, const void* k, const void* v, const void* o,
+                                       const float* lse, const void* dout, const void* dq,
+                                       const void* dk, const void* dv, const float* workspace, int B,
+                                       int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                                       fa_dtype_t dtype) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || d < 1) return FA_ERROR_INVALID_VALUE;
+    if (Hq % Hkv != 0) return FA_ERROR_INVALID_VALUE;
+    if (causal != 0 && causal != 1) return FA_ERROR_INVALID_VALUE;
+    if (!isfinite(scale)) return FA_ERROR_INVALID_VALUE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3 && dtype != FA_DTYPE_F32)
+        return FA_ERROR_INVALID_VALUE;
+    const int64_t q_elems = (int64_t)B * Hq * Nq * d;
+    const int64_t kv_elems = (int64_t)B * Hkv * Nk * d;
+    if (q_elems > kMaxElems || kv_elems > kMaxElems) return FA_ERROR_INVALID_VALUE;
+    if (q_elems > 0) {
+        if (q == nullptr || o == nullptr || dout == nullptr || dq == nullptr || lse == nullptr ||
+            workspace == nullptr)
+            return FA_ERROR_INVALID_VALUE;
+        if (!aligned(q, 16) || !aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+            !aligned(lse, 4) || !aligned(workspace, 4))
+            return FA_ERROR_INVALID_VALUE;
+    }
+    if (kv_elems > 0) {
+        if (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+            return FA_ERROR_INVALID_VALUE;
+    }
+    if (dtype != FA_DTYPE_BF16) return FA_ERROR_NOT_SUPPORTED;   // backward is bf16 only
+    if (d != 64 && d != 128) return FA_ERROR_NOT_SUPPORTED;
+    return FA_SUCCESS;
+}
+
+extern "C" fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, float* workspace, int B,
+                              int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                              fa_dtype_t dtype, hipStream_t stream) {
+    const fa_status_t st = fa_bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, Nq,
+                                           Nk, d, causal, scale, dtype);
+    if (st != FA_SUCCESS) return st;
+    if ((int64_t)B * Hq * Nq == 0 && (int64_t)B * Hkv * Nk == 0) return FA_SUCCESS;
+    fa::BwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.ws = workspace;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.group = Hq / Hkv;
+    p.causal_shift = Nk - Nq;
+    p.c = scale * fa::kLog2e;
+    p.scale = scale;
+    const hipError_t err = fa::launch_bwd(p, d, causal != 0, stream);
+    return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
+}
+

@@ -1,0 +1,516 @@
+// Backward pass of exact attention, bfloat16, head dim 64 or 128, gfx950.
+//
+// The backward pass recomputes the attention probabilities from the stored
+// per-row log-sum-exp instead of keeping P (page "Flash Attention",
+// 21medien.de, key techniques, recomputation).  With S = scale Q K^T + mask,
+// P = exp(S - LSE) row by row, and the upstream gradient dO:
+//   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D) with D_i = <dO_i, O_i>,
+//   dQ = scale dS K,   dK = scale dS^T Q
+// (D_i equals sum_j P_ij dP_ij, the row term of the softmax Jacobian).
+//
+// Three kernels on the caller's stream:
+//   1. fa_bwd_prep_kernel: D_i and the base-2 LSE per query row into the
+//      caller's workspace (a row that saw no key gets +inf, so its P is 0);
+//   2. fa_bwd_dkv_kernel: one workgroup owns 128 keys of one key/value head
+//      (32 per wave) and streams the Q and dO rows of every query head of
+//      its group through LDS in 32-row tiles; dK and dV accumulate in
+//      registers, so grouped-query sums need no atomics and the result is
+//      deterministic;
+//   3. fa_bwd_dq_kernel: one workgroup owns 128 query rows (32 per wave) and
+//      streams 32-key tiles of K and V, like the forward kernel.
+// Splitting dQ from dK/dV computes S and dP twice (7 products instead of 5)
+// but needs neither a float workspace for dQ nor atomics.
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16; lane l holds column l % 32 and rows
+// 8*(i/4) + 4*(l/32) + (i%4) of the 32x32 result, see fa_device.hpp):
+//   dQ kernel, per wave and 32-key tile:
+//     S^T = K Q^T, dP^T = V dO^T  (A: K / V rows from LDS, B: Q / dO rows in
+//                                   registers; lane = query)
+//     dQ^T += K^T dS^T            (A: K^T through ds_read_b64_tr_b16, B: dS
+//                                   from the score registers)
+//   dK/dV kernel, per wave and 32-query tile:
+//     S = Q K^T, dP = dO V^T      (A: Q / dO rows from LDS, B: K / V rows in
+//                                   registers; lane = key)
+//     dV^T += dO^T P, dK^T += Q^T dS   (A: transposing LDS reads of dO / Q)
+// Tiles are copied straight into LDS (global_load_lds_dwordx4), two stages,
+// XOR-swizzled in 16-byte units so the ds_read_b128 reads are conflict-free.
+#include <algorithm>
+#include <type_traits>
+
+#include "fa_bwd.hpp"
+#include "fa_device.hpp"
+
+namespace fa {
+
+namespace {
+
+template <int D>
+struct BwdCfg {
+    static constexpr int NW = 4;                  // waves per workgroup
+    static constexpr int ROWS = 128;              // query rows (dQ) or keys (dK/dV) per workgroup
+    static constexpr int T = 32;                  // rows per streamed tile
+    static constexpr int ROW = D * 2;             // bytes per row
+    static constexpr int UPR = D / 8;             // 16-byte units per row
+    static constexpr int KS = D / 16;             // MFMA steps over d
+    static constexpr int DB = D / 32;             // 32-wide blocks of d
+    static constexpr int TILE = T * ROW;          // bytes of one streamed tile of one tensor
+    static constexpr int STAGE = 2 * TILE;        // two tensors per stage
+    static constexpr int TILES = 2 * STAGE;       // two stages
+    static constexpr int SCRATCH = 256 * NW;      // per wave: 64 floats of row statistics (dK/dV kernel)
+    static constexpr int OUT = ROWS * ROW;        // epilogue staging of 128 output rows
+    static constexpr int LDS = TILES + SCRATCH > OUT ? TILES + SCRATCH : OUT;
+    static constexpr int CPW = TILE / 1024 / NW;  // 1 KiB copies per wave per tile and tensor
+    static constexpr int RPC = 1024 / ROW;        // rows per 1 KiB copy
+    // 16-byte-unit XOR swizzle of LDS rows: the 16 rows one ds_read_b128
+    // cycle touches cover all units (row mod 16 for 256-byte rows, (row/2)
+    // mod 8 for 128-byte rows, two of which share a bank sweep).  It is
+    // unchanged by a step of 16 rows.
+    __device__ static constexpr int swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+    static_assert(CPW >= 1, "a tile must give every wave a copy");
+};
+
+// Workgroup barrier without a memory fence; the tile copies are awaited with
+// vmcnt before it.  lgkmcnt(0) retires this wave's LDS reads of the stage the
+// next copies overwrite.
+__device__ __forceinline__ void bwd_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Copy rows r0 .. r0+31 of two [N, D] tensors (same layout, rows past N - 1
+// clamped to the last row) into an LDS stage: tensor a at dst, tensor b at
+// dst + TILE.  Every wave copies its CPW 1 KiB pieces of each.
+template <int D>
+__device__ __forceinline__ void copy_pair(const char* a, const char* b, int r0, int N, uint32_t dst,
+                                          int w, int lane) {
+    using C = BwdCfg<D>;
+    const int c_row = lane / C::UPR, c_su = lane % C::UPR;
+    const char* abase = a + (int64_t)r0 * C::ROW;
+    const char* bbase = b + (int64_t)r0 * C::ROW;
+    const int last = N - 1 - r0;
+#pragma unroll
+    for (int t = 0; t < C::CPW; ++t) {
+        const int piece = w * C::CPW + t;
+        const int row = piece * C::RPC + c_row;
+        const uint32_t off = min(row, last) * C::ROW + ((c_su ^ C::swz(row)) << 4);
+        dma16(abase, off, dst + piece * 1024);
+        dma16(bbase, off, dst + C::TILE + piece * 1024);
+    }
+}
+
+// Per-lane LDS offsets of a 32-row tile.
+template <int D>
+struct TileOffsets {
+    using C = BwdCfg<D>;
+    uint32_t b[C::KS];        // ds_read_b128 of row n, units 2*ks + g (MFMA A operand)
+    uint32_t lo[C::DB];       // transposing reads: row 4g + (n%16)/4 ...
+    uint32_t hi[C::DB];       // ... and 8 rows further; +16 rows per 16-row step
+    __device__ TileOffsets(int n, int g) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) b[ks] = n * C::ROW + (((2 * ks + g) ^ C::swz(n)) << 4);
+        const int tr_row = 4 * g + ((n & 15) >> 2);
+        const int tr_d = 16 * (n >> 4) + 4 * (n & 3);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const int d = 32 * db + tr_d;
+            lo[db] = tr_row * C::ROW + (((d >> 3) ^ C::swz(tr_row)) << 4) + (d & 7) * 2;
+            hi[db] = (tr_row + 8) * C::ROW + (((d >> 3) ^ C::swz(tr_row + 8)) << 4) + (d & 7) * 2;
+        }
+    }
+};
+
+// A operand of X^T (d-block db, 16-row step st) from a row-major tile in LDS.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const lds_char* tile, const TileOffsets<D>& off, int db, int st) {
+    using C = BwdCfg<D>;
+    const i16x4 lo = lds_tr16(tile + off.lo[db] + 16 * st * C::ROW);
+    const i16x4 hi = lds_tr16(tile + off.hi[db] + 16 * st * C::ROW);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The 16 accumulator values of a lane as two bf16 B operands (16-row steps).
+__device__ __forceinline__ void pack_b(const f32x16& v, bf16x8 (&out)[2]) {
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+        u32x4 pk;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) pk[e2] = pack_bf16x2(v[8 * h8 + 2 * e2], v[8 * h8 + 2 * e2 + 1]);
+        out[h8] = __builtin_bit_cast(bf16x8, pk);
+    }
+}
+
+// Row `row` of a [*, D] bf16 tensor as B operands (zeros past the end).
+template <int D>
+__device__ __forceinline__ void load_b_rows(const char* base, int row, int N, int g, bf16x8 (&f)[D / 16]) {
+    using C = BwdCfg<D>;
+    if (row < N) {
+        const char* src = base + (int64_t)row * C::ROW;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) f[ks] = __builtin_bit_cast(bf16x8, ldg16(src + (2 * ks + g) * 16));
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) f[ks] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+    }
+}
+
+// Scale 128 rows of fp32 accumulators (X^T blocks per wave: lane = row
+// 32*w + n, d = 32*db + 8*i4 + 4*g + r), convert to bf16, stage them in LDS
+// and write whole rows to dst with 16-byte coalesced stores.
+template <int D>
+__device__ __forceinline__ void store_rows(lds_char* smem, const f32x16 (&acc)[D / 32], float mul, char* dst,
+                                           int r0, int N, int w, int n, int g, int lane) {
+    using C = BwdCfg<D>;
+    __syncthreads();
+    const int row = w * 32 + n;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const int u = 4 * db + i4;
+            u32x2 val;
+            val[0] = pack_bf16x2(acc[db][4 * i4 + 0] * mul, acc[db][4 * i4 + 1] * mul);
+            val[1] = pack_bf16x2(acc[db][4 * i4 + 2] * mul, acc[db][4 * i4 + 3] * mul);
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                smem + row * C::ROW + ((u ^ C::swz(row)) << 4) + 8 * g) = val;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 32 * C::UPR / 64; ++it) {
+        const int f = it * 64 + lane;
+        const int r = w * 32 + f / C::UPR;
+        const int su = f % C::UPR;
+        const int grow = r0 + r;
+        if (grow < N) {
+            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(smem + r * C::ROW + su * 16);
+            *reinterpret_cast<u32x4*>(dst + (int64_t)grow * C::ROW + ((su ^ C::swz(r)) << 4)) = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- 1. D and base-2 LSE
+
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
+    constexpr int LPR = D / 8;          // lanes per row, 16 bytes each
+    constexpr int RPW = 64 / LPR;       // rows per wave per step
+    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+    const int64_t n_waves = ((int64_t)gridDim.x * 256) >> 6;
+    const int sub = lane / LPR, part = lane % LPR;
+    for (int64_t r0 = wave * RPW; r0 < R; r0 += n_waves * RPW) {
+        const int64_t r = r0 + sub;
+        float acc = 0.f;
+        if (r < R) {
+            const u32x4 a = ldg16(reinterpret_cast<const char*>(p.dout) + r * (D * 2) + part * 16);
+            const u32x4 o = ldg16(reinterpret_cast<const char*>(p.o) + r * (D * 2) + part * 16);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc += bf16_lo(a[k]) * bf16_lo(o[k]) + bf16_hi(a[k]) * bf16_hi(o[k]);
+        }
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+        if (part == 0 && r < R) {
+            p.ws[r] = acc;
+            const float l = p.lse[r];
+            p.ws[R + r] = l == -INFINITY ? INFINITY : l * kLog2e;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- 2. dK and dV
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdParams p) {
+    using C = BwdCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+    lds_char* smem = (lds_char*)smem_raw;
+    const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int g = lane >> 5;
+
+    // workgroup -> (batch, key/value head, key tile); the key tiles with the
+    // most visible queries (the first ones, for causal problems) come first
+    const int kvh = p.B * p.Hkv;
+    const int kt = blockIdx.x / kvh;
+    const int kvflat = blockIdx.x - kt * kvh;
+    const int b = kvflat / p.Hkv;
+    const int hkv = kvflat - b * p.Hkv;
+    const int k0 = kt * C::ROWS;
+    const int wk0 = k0 + 32 * w;
+    const int key = wk0 + n;
+
+    const int64_t kvrow0 = (int64_t)(b * p.Hkv + hkv) * p.Nk;
+    bf16x8 kf[C::KS], vf[C::KS];
+    load_b_rows<D>(reinterpret_cast<const char*>(p.k) + kvrow0 * C::ROW, key, p.Nk, g, kf);
+    load_b_rows<D>(reinterpret_cast<const char*>(p.v) + kvrow0 * C::ROW, key, p.Nk, g, vf);
+
+    // query tiles to visit, per query head of the group
+    const int qs = CAUSAL ? max(0, k0 - p.causal_shift) : 0;       // first query that sees key k0
+    const int qt0 = qs / C::T;
+    const int nqt = qs < p.Nq ? (p.Nq + C::T - 1) / C::T - qt0 : 0;
+    const int n_it = __builtin_amdgcn_readfirstlane(nqt * p.group);
+    const int wqs = __builtin_amdgcn_readfirstlane(CAUSAL ? max(0, wk0 - p.causal_shift) : 0);
+    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+
+    const TileOffsets<D> off(n, g);
+    float* scratch = reinterpret_cast<float*>(smem_raw + C::TILES + w * 256);
+
+    f32x16 dk[C::DB], dv[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    // Tile `it` = (query head hkv*group + it / nqt, query tile qt0 + it % nqt).
+    // Its copies go to LDS; this lane's share of its row statistics (lanes
+    // 0-31: base-2 LSE of row n, lanes 32-63: D of row n) to `pre`.
+    float pre = 0.f;
+    auto issue = [&](int it, int stage) {
+        const int gi = it / nqt;
+        const int qt = qt0 + (it - gi * nqt);
+        const int h = hkv * p.group + gi;
+        const int64_t qrow0 = (int64_t)(b * p.Hq + h) * p.Nq;
+        copy_pair<D>(reinterpret_cast<const char*>(p.q) + qrow0 * C::ROW,
+                     reinterpret_cast<const char*>(p.dout) + qrow0 * C::ROW, qt * C::T, p.Nq,
+                     smem_u32 + stage * C::STAGE, w, lane);
+        const int r = min(qt * C::T + n, p.Nq - 1);
+        pre = p.ws[(g ? 0 : R) + qrow0 + r];
+    };
+
+    auto tile = [&](auto stage_c, int it) {
+        constexpr int STG = decltype(stage_c)::value;
+        FA_WAIT_VMCNT(0);
+        bwd_barrier();
+        scratch[lane] = pre;                      // [0,32): base-2 LSE, [32,64): D
+        const int qt = qt0 + (it % nqt);
+        const int q0 = qt * C::T;
+        if (q0 + C::T - 1 < wqs) {                // no key of this wave is visible to these rows
+            if (it + 1 < n_it) issue(it + 1, STG ^ 1);
+            return;
+        }
+        const lds_char* qb = smem + STG * C::STAGE;
+        const lds_char* ob = qb + C::TILE;
+        f32x16 s = f32x16{}, dp = f32x16{};
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            s = mfma_bf16_32x32x16(lds_b128(qb + off.b[ks]), kf[ks], s);
+            dp = mfma_bf16_32x32x16(lds_b128(ob + off.b[ks]), vf[ks], dp);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        if (it + 1 < n_it) issue(it + 1, STG ^ 1);
+
+        // row statistics of the 16 query rows this lane holds
+        float l2[16], dl[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(scratch + 8 * a + 4 * g);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(scratch + 32 + 8 * a + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                l2[4 * a + r] = x[r];
+                dl[4 * a + r] = y[r];
+            }
+        }
+        const bool need_mask = (q0 + C::T > p.Nq) || (CAUSAL && wk0 + 31 > q0 + p.causal_shift);
+        f32x16 pv, ds;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float e = fast_exp2(fmaf(s[i], p.c, -l2[i]));
+            if (need_mask) {
+                const int qrow = q0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (qrow >= p.Nq || (CAUSAL && key > qrow + p.causal_shift)) e = 0.f;
+            }
+            pv[i] = e;
+            ds[i] = e * (dp[i] - dl[i]);
+        }
+        bf16x8 pp[2], pd[2];
+        pack_b(pv, pp);
+        pack_b(ds, pd);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+                dv[db] = mfma_bf16_32x32x16(tr_operand<D>(ob, off, db, st), pp[st], dv[db]);
+                dk[db] = mfma_bf16_32x32x16(tr_operand<D>(qb, off, db, st), pd[st], dk[db]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    if (n_it > 0) issue(0, 0);
+    for (int it = 0; it < n_it; it += 2) {
+        tile(std::integral_constant<int, 0>{}, it);
+        if (it + 1 < n_it) tile(std::integral_constant<int, 1>{}, it + 1);
+    }
+
+    char* dK = reinterpret_cast<char*>(p.dk) + kvrow0 * C::ROW;
+    char* dV = reinterpret_cast<char*>(p.dv) + kvrow0 * C::ROW;
+    store_rows<D>(smem, dk, p.scale, dK, k0, p.Nk, w, n, g, lane);
+    store_rows<D>(smem, dv, 1.f, dV, k0, p.Nk, w, n, g, lane);
+}
+
+// ---------------------------------------------------------------- 3. dQ
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
+    using C = BwdCfg<D>;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+    lds_char* smem = (lds_char*)smem_raw;
+    const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int g = lane >> 5;
+
+    // workgroup -> (batch, query head, query tile): heads first, and for
+    // causal problems the query tiles with the most keys first
+    const int n_heads = p.B * p.Hq;
+    const int t_ord = blockIdx.x / n_heads;
+    const int x = blockIdx.x - t_ord * n_heads;
+    const int kvh = p.B * p.Hkv;
+    const int kvflat = x % kvh;
+    const int gi = x / kvh;
+    const int b = kvflat / p.Hkv;
+    const int hkv = kvflat - b * p.Hkv;
+    const int hq = hkv * p.group + gi;
+    const int qt = CAUSAL ? p.n_qtiles - 1 - t_ord : t_ord;
+    const int q0 = qt * C::ROWS;
+    const int wq0 = q0 + 32 * w;
+    const int qrow = wq0 + n;
+
+    const int64_t qrow0 = (int64_t)(b * p.Hq + hq) * p.Nq;
+    const int64_t kvrow0 = (int64_t)(b * p.Hkv + hkv) * p.Nk;
+    const char* Kh = reinterpret_cast<const char*>(p.k) + kvrow0 * C::ROW;
+    const char* Vh = reinterpret_cast<const char*>(p.v) + kvrow0 * C::ROW;
+
+    int kend = p.Nk;
+    if (CAUSAL) kend = min(kend, max(q0 + C::ROWS + p.causal_shift, 0));
+    const int n_tiles = __builtin_amdgcn_readfirstlane((kend + C::T - 1) / C::T);
+    int wkend = p.Nk;
+    if (CAUSAL) wkend = min(wkend, max(wq0 + 32 + p.causal_shift, 0));
+    wkend = __builtin_amdgcn_readfirstlane(wkend);
+
+    bf16x8 qf[C::KS], df[C::KS];
+    load_b_rows<D>(reinterpret_cast<const char*>(p.q) + qrow0 * C::ROW, qrow, p.Nq, g, qf);
+    load_b_rows<D>(reinterpret_cast<const char*>(p.dout) + qrow0 * C::ROW, qrow, p.Nq, g, df);
+    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+    float lse2 = INFINITY, dlt = 0.f;
+    if (qrow < p.Nq) {
+        dlt = p.ws[qrow0 + qrow];
+        lse2 = p.ws[R + qrow0 + qrow];
+    }
+
+    const TileOffsets<D> off(n, g);
+    f32x16 acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+    auto issue = [&](int j, int stage) {
+        copy_pair<D>(Kh, Vh, j * C::T, p.Nk, smem_u32 + stage * C::STAGE, w, lane);
+    };
+
+    auto tile = [&](auto stage_c, int j) {
+        constexpr int STG = decltype(stage_c)::value;
+        FA_WAIT_VMCNT(0);
+        bwd_barrier();
+        const int key0 = j * C::T;
+        if (key0 >= wkend) {                      // every key of the tile is hidden from this wave
+            if (j + 1 < n_tiles) issue(j + 1, STG ^ 1);
+            return;
+        }
+        const lds_char* kb = smem + STG * C::STAGE;
+        const lds_char* vb = kb + C::TILE;
+        f32x16 s = f32x16{}, dp = f32x16{};
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            s = mfma_bf16_32x32x16(lds_b128(kb + off.b[ks]), qf[ks], s);
+            dp = mfma_bf16_32x32x16(lds_b128(vb + off.b[ks]), df[ks], dp);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        if (j + 1 < n_tiles) issue(j + 1, STG ^ 1);
+
+        const bool need_mask = (key0 + C::T > p.Nk) || (CAUSAL && key0 + C::T - 1 > wq0 + p.causal_shift);
+        const int lim = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - key0 - 4 * g;
+        f32x16 ds;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float e = fast_exp2(fmaf(s[i], p.c, -lse2));
+            if (need_mask && 8 * (i >> 2) + (i & 3) > lim) e = 0.f;
+            ds[i] = e * (dp[i] - dlt);
+        }
+        bf16x8 pd[2];
+        pack_b(ds, pd);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) acc[db] = mfma_bf16_32x32x16(tr_operand<D>(kb, off, db, st), pd[st], acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    if (n_tiles > 0) issue(0, 0);
+    for (int j = 0; j < n_tiles; j += 2) {
+        tile(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, j + 1);
+    }
+
+    store_rows<D>(smem, acc, p.scale, reinterpret_cast<char*>(p.dq) + qrow0 * C::ROW, q0, p.Nq, w, n, g, lane);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+    using C = BwdCfg<D>;
+    BwdParams pp = p;
+    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+    void* args[] = {&pp};
+    hipError_t e = hipSuccess;
+    if (R > 0) {
+        const int64_t rows_per_block = 4 * (64 / (D / 8));
+        const int64_t blocks = std::min<int64_t>((R + rows_per_block - 1) / rows_per_block, 4096);
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_prep_kernel<D>), dim3((unsigned)blocks),
+                            dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    pp.n_ktiles = (p.Nk + C::ROWS - 1) / C::ROWS;
+    const int64_t kv_grid = (int64_t)pp.n_ktiles * p.B * p.Hkv;
+    if (kv_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    if (kv_grid > 0) {
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL>), dim3((unsigned)kv_grid),
+                            dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    pp.n_qtiles = (p.Nq + C::ROWS - 1) / C::ROWS;
+    const int64_t q_grid = (int64_t)pp.n_qtiles * p.B * p.Hq;
+    if (q_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    if (q_grid > 0)
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)q_grid),
+                            dim3(256), args, 0, stream);
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+    if (d == 64) return causal ? launch_bwd_d<64, true>(p, stream) : launch_bwd_d<64, false>(p, stream);
+    if (d == 128) return causal ? launch_bwd_d<128, true>(p, stream) : launch_bwd_d<128, false>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

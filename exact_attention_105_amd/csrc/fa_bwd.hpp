@@ -1,0 +1,31 @@
+// Host/device interface of the attention backward kernels (fa_bwd.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct BwdParams {
+    const void* q;       // [B, Hq, Nq, d] bf16
+    const void* k;       // [B, Hkv, Nk, d] bf16
+    const void* v;       // [B, Hkv, Nk, d] bf16
+    const void* o;       // [B, Hq, Nq, d] bf16, the forward output
+    const float* lse;    // [B, Hq, Nq], the forward log-sum-exp (natural log)
+    const void* dout;    // [B, Hq, Nq, d] bf16, gradient of the output
+    void* dq;            // [B, Hq, Nq, d] bf16
+    void* dk;            // [B, Hkv, Nk, d] bf16
+    void* dv;            // [B, Hkv, Nk, d] bf16
+    float* ws;           // 2 * B * Hq * Nq floats: delta, then the log2-domain LSE
+    int B, Hq, Hkv, Nq, Nk;
+    int group;           // Hq / Hkv
+    int causal_shift;    // Nk - Nq: key j visible to query i iff j <= i + causal_shift
+    int n_qtiles;        // dQ kernel: query tiles per head
+    int n_ktiles;        // dK/dV kernel: key tiles per key/value head
+    float c;             // scale * log2(e), signed
+    float scale;         // multiplies dQ and dK
+};
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
+
+}  // namespace fa

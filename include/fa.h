@@ -140,6 +140,47 @@ fa_status_t fa_rotate_quantize_validate(const void* x, fa_dtype_t x_dtype, long 
                                         int rotate, const unsigned char* codes, const float* scale,
                                         const float* work);
 
+/*
+ * fa_bwd -- backward pass of fa_fwd (bf16), asynchronous on `stream`.
+ *
+ * Given the forward inputs q, k, v, the forward outputs o and lse (as
+ * written by fa_fwd with the same arguments) and the gradient dout of a loss
+ * with respect to o, writes the gradients dq, dk, dv.  Attention
+ * probabilities are recomputed from q, k and lse, not stored (page "Flash
+ * Attention", 21medien.de, key techniques, recomputation).  With
+ * S = scale q k^T + mask and P = exp(S - lse) row by row:
+ *   dv = P^T dout,  dP = dout v^T,  dS = P * (dP - D) with D_i = <dout_i, o_i>,
+ *   dq = scale dS k,  dk = scale dS^T q,
+ * where a key/value head's dk and dv sum over every query head that reads
+ * it.  Masking, head grouping and the bottom-right causal alignment are those
+ * of fa_fwd; rows that see no key (lse = -inf) contribute nothing.
+ *
+ * Pointers (device memory, owned by the caller; layouts as in fa_fwd):
+ *   q, o, dout, dq   [B, Hq, Nq, d] bf16, aligned to 16 bytes
+ *   k, v, dk, dv     [B, Hkv, Nk, d] bf16, aligned to 16 bytes
+ *   lse              [B, Hq, Nq] fp32
+ *   workspace        2 * B * Hq * Nq floats the call overwrites (D and a
+ *                    base-2 copy of lse); calls that share it must be ordered
+ * dq, dk and dv are written in full (keys no query sees get zero gradients).
+ * dtype must be FA_DTYPE_BF16; d in {64, 128}; other sizes as in fa_fwd.
+ *
+ * Returns FA_SUCCESS once the kernels are enqueued, FA_ERROR_INVALID_VALUE
+ * for a null or misaligned pointer or an out-of-range size,
+ * FA_ERROR_NOT_SUPPORTED for another dtype or d, FA_ERROR_LAUNCH_FAILURE if a
+ * launch fails.  On an argument error nothing is launched.  No device memory
+ * is allocated.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, float* workspace, int B, int Hq,
+                   int Hkv, int Nq, int Nk, int d, int causal, float scale, fa_dtype_t dtype,
+                   hipStream_t stream);
+
+/* The argument checks of fa_bwd as a pure host function. */
+fa_status_t fa_bwd_validate(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, const void* dq, const void* dk,
+                            const void* dv, const float* workspace, int B, int Hq, int Hkv, int Nq,
+                            int Nk, int d, int causal, float scale, fa_dtype_t dtype);
+
 /* A static, human-readable description of a status code. */
 const char* fa_status_string(fa_status_t status);
 

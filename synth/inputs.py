@@ -200,3 +200,10 @@ def make_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed, *, outlier_mult: float = 20.
     kc, sk = quantise_e4m3(kf)
     vc, sv = quantise_e4m3(vf)
     return {"q": qc, "k": kc, "v": vc, "descale": (float(sq), float(sk), float(sv))}
+
+
+def make_grad_output(B, Hq, Nq, d, seed):
+    """The upstream gradient dO of a backward-pass workload: float32 standard
+    normals from PCG64(seed + 1000), rounded to bfloat16 (uint16 bits)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    return f32_to_bf16_bits(normals(rng, (B, Hq, Nq, d)))

@@ -131,3 +131,46 @@ def test_rotate_unsupported(lib, kw):
 def test_fwd_rejects_fp32_attention(lib):
     assert validate(dtype=_lib.FA_DTYPE_F32) == _lib.FA_ERROR_NOT_SUPPORTED
     assert validate(dtype=_lib.FA_DTYPE_F32, descale=(1.0, 1.0, 1.0)) == _lib.FA_ERROR_INVALID_VALUE
+
+
+# ---------------------------------------------------------------- fa_bwd
+BGOOD = dict(q=4096, k=8192, v=12288, o=16384, lse=20480, do=24576, dq=28672, dk=32768, dv=36864,
+             ws=40960, B=2, Hq=8, Hkv=2, Nq=100, Nk=77, d=128, causal=1, scale=0.125,
+             dtype=_lib.FA_DTYPE_BF16)
+
+
+def bvalidate(**kw):
+    a = dict(BGOOD)
+    a.update(kw)
+    return _lib.fa_bwd_validate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                a["ws"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                                a["scale"], a["dtype"])
+
+
+def test_bwd_valid_arguments(lib):
+    assert bvalidate() == _lib.FA_SUCCESS
+    assert bvalidate(d=64, causal=0, Hkv=8) == _lib.FA_SUCCESS
+    assert bvalidate(scale=-0.5) == _lib.FA_SUCCESS
+    # no query rows: the query-side pointers may be null
+    assert bvalidate(Nq=0, q=None, o=None, lse=None, do=None, dq=None, ws=None) == _lib.FA_SUCCESS
+    # no keys: the key-side pointers may be null
+    assert bvalidate(Nk=0, k=None, v=None, dk=None, dv=None) == _lib.FA_SUCCESS
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=-1), dict(Hq=0), dict(Hkv=3), dict(Nq=-1), dict(Nk=-2), dict(d=0), dict(causal=2),
+    dict(scale=math.inf), dict(scale=math.nan), dict(dtype=7),
+    dict(q=None), dict(o=None), dict(lse=None), dict(do=None), dict(dq=None), dict(ws=None),
+    dict(k=None), dict(v=None), dict(dk=None), dict(dv=None),
+    dict(q=4096 + 8), dict(do=24576 + 2), dict(dq=28672 + 4), dict(dk=32768 + 8), dict(dv=36864 + 1),
+    dict(lse=20480 + 2), dict(ws=40960 + 1),
+    dict(B=1, Hq=1, Hkv=1, Nq=1 << 24, d=128),
+])
+def test_bwd_invalid_arguments(lib, kw):
+    assert bvalidate(**kw) == _lib.FA_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=256), dict(dtype=_lib.FA_DTYPE_FP8_E4M3),
+                                dict(dtype=_lib.FA_DTYPE_F32)])
+def test_bwd_unsupported(lib, kw):
+    assert bvalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
