@@ -263,6 +263,102 @@ def rotate_bench(args):
                       "cpu_baseline": cpu}), flush=True)
 
 
+def bwd_bench(args):
+    """One fa_bwd call per step on the workload's shape (bf16): dQ, dK, dV
+    from Q, K, V, the forward's O and LSE, and a seeded dO.  The metric
+    counts 2.5x the forward FLOPs (the five products of the textbook backward:
+    S, dP, dV, dK, dQ); the kernels recompute S and dP in both the dK/dV and
+    the dQ kernel, 3.5x in all, which the line reports as mfma_flops_per_step."""
+    import torch
+    from exact_attention_105_amd import bwd, fwd, load
+    from synth.inputs import CONFIGS, generate, make_grad_output
+
+    load()
+    cfg = CONFIGS[args.config]
+    if cfg.dtype != "bf16":
+        raise SystemExit("the backward pass is bf16 only")
+    x = generate(cfg)
+    dob = make_grad_output(cfg.B, cfg.Hq, cfg.Nq, cfg.d, cfg.seed)
+    dev = torch.device("cuda:0")
+    conv = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, do = conv(x["q"]), conv(x["k"]), conv(x["v"]), conv(dob)
+    o, lse = fwd(q, k, v, causal=cfg.causal, scale=cfg.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(2 * cfg.B * cfg.Hq * cfg.Nq, 1), dtype=torch.float32, device=dev)
+
+    def step():
+        bwd(q, k, v, o, lse, do, causal=cfg.causal, scale=cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = 2.5 * cfg.flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = bwd_cpu_baseline(cfg, x, dob, args.cpu_budget)
+    print(json.dumps({
+        "metric": "attention backward TFLOP/s (2.5x forward FLOPs) on 1 MI355X", "value": tflops,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs and dO)",
+        "config": {"workload": cfg.name + " backward", "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Nq": cfg.Nq,
+                   "Nk": cfg.Nk, "d": cfg.d, "causal": cfg.causal, "flops_per_step": flops,
+                   "mfma_flops_per_step": 3.5 * cfg.flops, "kernel_source_hash": bwd_source_hash()},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
+                     "traffic": None, "scope": "one fa_bwd call (prep, dK/dV and dQ kernels)"},
+        "cpu_baseline": cpu}), flush=True)
+
+
+def bwd_source_hash() -> str:
+    from exact_attention_105_amd import build as _build
+    csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("fa_bwd.hip", "fa_bwd.hpp", "fa_device.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + _code_only(fh.read()))
+    h.update(" ".join(_build.HIPCC_FLAGS + _build.SOURCE_FLAGS.get("fa_bwd.hip", [])).encode())
+    return h.hexdigest()[:16]
+
+
+def bwd_cpu_baseline(cfg, x, dob, budget_s: float):
+    """The oracle's row-local dQ (S, dP and dQ rows: 6 * visible keys * d
+    flops per row) on sampled query rows of the workload, for about budget_s
+    seconds."""
+    import oracle
+    rng = np.random.default_rng(777)
+    total = cfg.B * cfg.Hq * cfg.Nq
+    n = 8
+    while True:
+        rows = np.sort(rng.choice(total, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.bwd_dq_rows(x["q"], x["k"], x["v"], dob, causal=cfg.causal, scale=cfg.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= 0.1 * budget_s or n >= total:
+            break
+        n = min(total, n * 4)
+    n = int(min(total, max(n, n * budget_s / max(dt, 1e-9))))
+    rows = np.sort(rng.choice(total, size=n, replace=False))
+    t0 = time.perf_counter()
+    oracle.bwd_dq_rows(x["q"], x["k"], x["v"], dob, causal=cfg.causal, scale=cfg.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    i = rows % cfg.Nq
+    vis = np.minimum(cfg.Nk, i + cfg.Nk - cfg.Nq + 1) if cfg.causal else np.full(n, cfg.Nk)
+    flops = float(np.sum(6.0 * np.maximum(vis, 0) * cfg.d))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"row-local dQ of {n} sampled query rows ({dt:.1f} s)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,6 +371,8 @@ def main():
                     help="instead of attention, time a bf16 n x n x n torch.matmul (vendor GEMM context)")
     ap.add_argument("--rotate", action="store_true",
                     help="instead of attention, time the Hadamard rotation + E4M3 quantisation step")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (fa_bwd) on --config instead of the forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
@@ -285,13 +383,16 @@ def main():
     if args.gemm_reference > 0:
         gemm_reference(args)
         return
-    if args.rotate:
-        rotate_bench(args)
-        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.rotate:
+        rotate_bench(args)
+        return
+    if args.bwd:
+        bwd_bench(args)
+        return
 
     import torch
     from exact_attention_105_amd import fwd, load
