@@ -40,6 +40,10 @@
 #include "fa_bwd.hpp"
 #include "fa_device.hpp"
 
+#ifndef FA_BWD_DKV_HALVES
+#define FA_BWD_DKV_HALVES 2
+#endif
+
 namespace fa {
 
 namespace {
@@ -48,7 +52,11 @@ template <int D>
 struct BwdCfg {
     static constexpr int NW = 4;                  // waves per workgroup
     static constexpr int ROWS = 128;              // query rows (dQ) or keys (dK/dV) per workgroup
-    static constexpr int T = 32;                  // rows per streamed tile
+    static constexpr int T = 32;                  // keys per streamed tile (dQ kernel)
+    static constexpr int NH = FA_BWD_DKV_HALVES;  // 32-row query halves per tile (dK/dV kernel)
+    static constexpr int TQ = 32 * NH;            // query rows per streamed tile (dK/dV kernel)
+    static constexpr int QSTAGE = 2 * TQ * D * 2; // Q tile + dO tile
+    static constexpr int QTILES = 2 * QSTAGE;     // two stages
     static constexpr int ROW = D * 2;             // bytes per row
     static constexpr int UPR = D / 8;             // 16-byte units per row
     static constexpr int KS = D / 16;             // MFMA steps over d
@@ -56,17 +64,16 @@ struct BwdCfg {
     static constexpr int TILE = T * ROW;          // bytes of one streamed tile of one tensor
     static constexpr int STAGE = 2 * TILE;        // two tensors per stage
     static constexpr int TILES = 2 * STAGE;       // two stages
-    static constexpr int SCRATCH = 256 * NW;      // per wave: 64 floats of row statistics (dK/dV kernel)
+    static constexpr int SCRATCH = 8 * TQ * NW;   // per wave: 2 * TQ floats of row statistics (dK/dV kernel)
     static constexpr int OUT = ROWS * ROW;        // epilogue staging of 128 output rows
-    static constexpr int LDS = TILES + SCRATCH > OUT ? TILES + SCRATCH : OUT;
-    static constexpr int CPW = TILE / 1024 / NW;  // 1 KiB copies per wave per tile and tensor
+    static constexpr int LDS = TILES > OUT ? TILES : OUT;                       // dQ kernel
+    static constexpr int LDS_KV = QTILES + SCRATCH > OUT ? QTILES + SCRATCH : OUT;   // dK/dV kernel
     static constexpr int RPC = 1024 / ROW;        // rows per 1 KiB copy
     // 16-byte-unit XOR swizzle of LDS rows: the 16 rows one ds_read_b128
     // cycle touches cover all units (row mod 16 for 256-byte rows, (row/2)
     // mod 8 for 128-byte rows, two of which share a bank sweep).  It is
     // unchanged by a step of 16 rows.
     __device__ static constexpr int swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-    static_assert(CPW >= 1, "a tile must give every wave a copy");
 };
 
 // Workgroup barrier without a memory fence; the tile copies are awaited with
@@ -79,24 +86,27 @@ __device__ __forceinline__ void bwd_barrier() {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Copy rows r0 .. r0+31 of two [N, D] tensors (same layout, rows past N - 1
-// clamped to the last row) into an LDS stage: tensor a at dst, tensor b at
-// dst + TILE.  Every wave copies its CPW 1 KiB pieces of each.
-template <int D>
+// Copy rows r0 .. r0+NR-1 of two [N, D] tensors (same layout, rows past
+// N - 1 clamped to the last row) into an LDS stage: tensor a at dst, tensor b
+// at dst + NR rows.  Every wave copies its share of the 1 KiB pieces of each.
+template <int D, int NR>
 __device__ __forceinline__ void copy_pair(const char* a, const char* b, int r0, int N, uint32_t dst,
                                           int w, int lane) {
     using C = BwdCfg<D>;
+    constexpr int BYTES = NR * C::ROW;
+    constexpr int PW = BYTES / 1024 / C::NW;      // pieces per wave and tensor
+    static_assert(PW >= 1, "a tile must give every wave a copy");
     const int c_row = lane / C::UPR, c_su = lane % C::UPR;
     const char* abase = a + (int64_t)r0 * C::ROW;
     const char* bbase = b + (int64_t)r0 * C::ROW;
     const int last = N - 1 - r0;
 #pragma unroll
-    for (int t = 0; t < C::CPW; ++t) {
-        const int piece = w * C::CPW + t;
+    for (int t = 0; t < PW; ++t) {
+        const int piece = w * PW + t;
         const int row = piece * C::RPC + c_row;
         const uint32_t off = min(row, last) * C::ROW + ((c_su ^ C::swz(row)) << 4);
         dma16(abase, off, dst + piece * 1024);
-        dma16(bbase, off, dst + C::TILE + piece * 1024);
+        dma16(bbase, off, dst + BYTES + piece * 1024);
     }
 }
 
@@ -224,7 +234,8 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdParams p) {
     using C = BwdCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
+    constexpr int NH = C::NH, TQ = C::TQ;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_KV];
     lds_char* smem = (lds_char*)smem_raw;
     const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
     const int tid = threadIdx.x;
@@ -251,14 +262,14 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
 
     // query tiles to visit, per query head of the group
     const int qs = CAUSAL ? max(0, k0 - p.causal_shift) : 0;       // first query that sees key k0
-    const int qt0 = qs / C::T;
-    const int nqt = qs < p.Nq ? (p.Nq + C::T - 1) / C::T - qt0 : 0;
+    const int qt0 = qs / TQ;
+    const int nqt = qs < p.Nq ? (p.Nq + TQ - 1) / TQ - qt0 : 0;
     const int n_it = __builtin_amdgcn_readfirstlane(nqt * p.group);
     const int wqs = __builtin_amdgcn_readfirstlane(CAUSAL ? max(0, wk0 - p.causal_shift) : 0);
     const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
 
     const TileOffsets<D> off(n, g);
-    float* scratch = reinterpret_cast<float*>(smem_raw + C::TILES + w * 256);
+    float* scratch = reinterpret_cast<float*>(smem_raw + C::QTILES + w * 8 * TQ);
 
     f32x16 dk[C::DB], dv[C::DB];
 #pragma unroll
@@ -268,84 +279,102 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
     }
 
     // Tile `it` = (query head hkv*group + it / nqt, query tile qt0 + it % nqt).
-    // Its copies go to LDS; this lane's share of its row statistics (lanes
-    // 0-31: base-2 LSE of row n, lanes 32-63: D of row n) to `pre`.
-    float pre = 0.f;
+    // Its copies go to LDS; the row statistics of its TQ rows to `pre`
+    // (pre[h]: lanes 0-31 the base-2 LSE of row 32h + n, lanes 32-63 its D).
+    float pre[NH];
     auto issue = [&](int it, int stage) {
         const int gi = it / nqt;
         const int qt = qt0 + (it - gi * nqt);
         const int h = hkv * p.group + gi;
         const int64_t qrow0 = (int64_t)(b * p.Hq + h) * p.Nq;
-        copy_pair<D>(reinterpret_cast<const char*>(p.q) + qrow0 * C::ROW,
-                     reinterpret_cast<const char*>(p.dout) + qrow0 * C::ROW, qt * C::T, p.Nq,
-                     smem_u32 + stage * C::STAGE, w, lane);
-        const int r = min(qt * C::T + n, p.Nq - 1);
-        pre = p.ws[(g ? 0 : R) + qrow0 + r];
+        copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qrow0 * C::ROW,
+                         reinterpret_cast<const char*>(p.dout) + qrow0 * C::ROW, qt * TQ, p.Nq,
+                         smem_u32 + stage * C::QSTAGE, w, lane);
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+            const int r = min(qt * TQ + 32 * hh + n, p.Nq - 1);
+            pre[hh] = p.ws[(g ? 0 : R) + qrow0 + r];
+        }
     };
 
     auto tile = [&](auto stage_c, int it) {
         constexpr int STG = decltype(stage_c)::value;
         FA_WAIT_VMCNT(0);
         bwd_barrier();
-        scratch[lane] = pre;                      // [0,32): base-2 LSE, [32,64): D
+        // scratch: [0, TQ) base-2 LSE, [TQ, 2 TQ) D of the tile's rows
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) scratch[(g ? TQ : 0) + 32 * hh + n] = pre[hh];
         const int qt = qt0 + (it % nqt);
-        const int q0 = qt * C::T;
-        if (q0 + C::T - 1 < wqs) {                // no key of this wave is visible to these rows
+        const int q0 = qt * TQ;
+        if (q0 + TQ - 1 < wqs) {                  // no key of this wave is visible to these rows
             if (it + 1 < n_it) issue(it + 1, STG ^ 1);
             return;
         }
-        const lds_char* qb = smem + STG * C::STAGE;
-        const lds_char* ob = qb + C::TILE;
-        f32x16 s = f32x16{}, dp = f32x16{};
+        const lds_char* qb = smem + STG * C::QSTAGE;
+        const lds_char* ob = qb + TQ * C::ROW;
+        // S and dP of every half first: the MFMA pipe works through the later
+        // halves while the first half's exponentials run on the VALU
+        f32x16 s[NH], dp[NH];
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            s = mfma_bf16_32x32x16(lds_b128(qb + off.b[ks]), kf[ks], s);
-            dp = mfma_bf16_32x32x16(lds_b128(ob + off.b[ks]), vf[ks], dp);
+        for (int hh = 0; hh < NH; ++hh) {
+            s[hh] = f32x16{};
+            dp[hh] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                s[hh] = mfma_bf16_32x32x16(lds_b128(qb + 32 * hh * C::ROW + off.b[ks]), kf[ks], s[hh]);
+                dp[hh] = mfma_bf16_32x32x16(lds_b128(ob + 32 * hh * C::ROW + off.b[ks]), vf[ks], dp[hh]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (it + 1 < n_it) issue(it + 1, STG ^ 1);
 
-        // row statistics of the 16 query rows this lane holds
-        float l2[16], dl[16];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(scratch + 8 * a + 4 * g);
-            const f32x4 y = *reinterpret_cast<const f32x4*>(scratch + 32 + 8 * a + 4 * g);
+        for (int hh = 0; hh < NH; ++hh) {
+            const int q0h = q0 + 32 * hh;
+            // row statistics of the 16 query rows this lane holds
+            float l2[16], dl[16];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                l2[4 * a + r] = x[r];
-                dl[4 * a + r] = y[r];
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(scratch + 32 * hh + 8 * a + 4 * g);
+                const f32x4 y = *reinterpret_cast<const f32x4*>(scratch + TQ + 32 * hh + 8 * a + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    l2[4 * a + r] = x[r];
+                    dl[4 * a + r] = y[r];
+                }
             }
+            const bool need_mask = (q0h + 32 > p.Nq) || (CAUSAL && wk0 + 31 > q0h + p.causal_shift);
+            f32x16 pv, ds;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float e = fast_exp2(fmaf(s[hh][i], p.c, -l2[i]));
+                if (need_mask) {
+                    const int qrow = q0h + 8 * (i >> 2) + 4 * g + (i & 3);
+                    if (qrow >= p.Nq || (CAUSAL && key > qrow + p.causal_shift)) e = 0.f;
+                }
+                pv[i] = e;
+                ds[i] = e * (dp[hh][i] - dl[i]);
+            }
+            bf16x8 pp[2], pd[2];
+            pack_b(pv, pp);
+            pack_b(ds, pd);
+            const lds_char* qbh = qb + 32 * hh * C::ROW;
+            const lds_char* obh = ob + 32 * hh * C::ROW;
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) {
+                    dv[db] = mfma_bf16_32x32x16(tr_operand<D>(obh, off, db, st), pp[st], dv[db]);
+                    dk[db] = mfma_bf16_32x32x16(tr_operand<D>(qbh, off, db, st), pd[st], dk[db]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
         }
-        const bool need_mask = (q0 + C::T > p.Nq) || (CAUSAL && wk0 + 31 > q0 + p.causal_shift);
-        f32x16 pv, ds;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float e = fast_exp2(fmaf(s[i], p.c, -l2[i]));
-            if (need_mask) {
-                const int qrow = q0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (qrow >= p.Nq || (CAUSAL && key > qrow + p.causal_shift)) e = 0.f;
-            }
-            pv[i] = e;
-            ds[i] = e * (dp[i] - dl[i]);
-        }
-        bf16x8 pp[2], pd[2];
-        pack_b(pv, pp);
-        pack_b(ds, pd);
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                dv[db] = mfma_bf16_32x32x16(tr_operand<D>(ob, off, db, st), pp[st], dv[db]);
-                dk[db] = mfma_bf16_32x32x16(tr_operand<D>(qb, off, db, st), pd[st], dk[db]);
-            }
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(0);
     };
 
     if (n_it > 0) issue(0, 0);
@@ -418,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
     auto issue = [&](int j, int stage) {
-        copy_pair<D>(Kh, Vh, j * C::T, p.Nk, smem_u32 + stage * C::STAGE, w, lane);
+        copy_pair<D, C::T>(Kh, Vh, j * C::T, p.Nk, smem_u32 + stage * C::STAGE, w, lane);
     };
 
     auto tile = [&](auto stage_c, int j) {
