@@ -316,8 +316,19 @@ def bwd_bench(args):
                    "Nk": cfg.Nk, "d": cfg.d, "causal": cfg.causal, "flops_per_step": flops,
                    "mfma_flops_per_step": 3.5 * cfg.flops, "kernel_source_hash": bwd_source_hash()},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
-                     "traffic": None, "scope": "one fa_bwd call (prep, dK/dV and dQ kernels)"},
+                     "traffic": load_bwd_traffic(cfg), "scope": "one fa_bwd call (prep, dK/dV and dQ kernels)"},
         "cpu_baseline": cpu}), flush=True)
+
+
+def load_bwd_traffic(cfg):
+    """HBM bytes per fa_bwd call from the committed counter summary, if taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_bwd_{cfg.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return t.get("hbm_bytes_per_call") if t.get("kernel_source_hash") == bwd_source_hash() else None
 
 
 def bwd_source_hash() -> str:
