@@ -70,6 +70,49 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     return out, lse
 
 
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+               cu_seqlens_k: torch.Tensor, max_seqlen_q: int, *, causal: bool = False,
+               scale: float | None = None, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Exact attention over a packed batch of variable-length sequences.
+
+    q [total_q, Hq, d], k and v [total_k, Hkv, d] (bfloat16, contiguous, one
+    GPU); cu_seqlens_q / cu_seqlens_k int32 GPU tensors of n_seqs + 1
+    offsets; max_seqlen_q at least every query length.  Returns (O
+    [total_q, Hq, d] bfloat16, LSE [Hq, total_q] float32).  Runs on torch's
+    current stream.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dim() != 3 or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 [tokens, H, d] GPU tensor")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda or t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU vector")
+    n_seqs = cu_seqlens_q.numel() - 1
+    if n_seqs < 0 or cu_seqlens_k.numel() != n_seqs + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold n_seqs + 1 offsets")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk_ = k.shape
+    if dk_ != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((total_q, Hq, d), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (total_q, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [total_q, Hq, d] tensor")
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), n_seqs, int(max_seqlen_q),
+                            total_q, total_k, Hq, Hkv, d, int(bool(causal)), scale, _lib.FA_DTYPE_BF16, stream)
+    if st != _lib.FA_SUCCESS:
+        raise _lib.FaError(st, _lib.status_string(st))
+    return out, lse
+
+
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
         dout: torch.Tensor, *, causal: bool = False, scale: float | None = None,
         dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,

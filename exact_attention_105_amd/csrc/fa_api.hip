@@ -7,6 +7,7 @@
 #include "fa.h"
 #include "fa_bwd.hpp"
 #include "fa_launch.hpp"
+#include "fa_varlen.hpp"
 
 namespace {
 
@@ -214,6 +215,77 @@ extern "C" fa_status_t fa_bwd(const void* q, const void* k, const void* v, const
     p.c = scale * fa::kLog2e;
     p.scale = scale;
     const hipError_t err = fa::launch_bwd(p, d, causal != 0, stream);
+    return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
+}
+
+extern "C" fa_status_t fa_fwd_varlen_validate(const void* q, const void* k, const void* v, const void* o,
+                                              const float* lse, const int* cu_seqlens_q,
+                                              const int* cu_seqlens_k, int n_seqs, int max_seqlen_q,
+                                              int total_q, int total_k, int Hq, int Hkv, int d, int causal,
+                                              float scale, fa_dtype_t dtype) {
+    if (n_seqs < 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0 || Hq < 1 || Hkv < 1 || d < 1)
+        return FA_ERROR_INVALID_VALUE;
+    if (Hq % Hkv != 0) return FA_ERROR_INVALID_VALUE;
+    if (causal != 0 && causal != 1) return FA_ERROR_INVALID_VALUE;
+    if (!isfinite(scale)) return FA_ERROR_INVALID_VALUE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3 && dtype != FA_DTYPE_F32)
+        return FA_ERROR_INVALID_VALUE;
+    const int64_t q_elems = (int64_t)total_q * Hq * d;
+    const int64_t kv_elems = (int64_t)total_k * Hkv * d;
+    if (q_elems > kMaxElems || kv_elems > kMaxElems) return FA_ERROR_INVALID_VALUE;
+    // the grid covers max_seqlen_q rows of every sequence and query head
+    if ((int64_t)((max_seqlen_q + 127) / 128) * n_seqs * Hq > 0x7FFFFFFFLL) return FA_ERROR_INVALID_VALUE;
+    if (n_seqs > 0) {
+        if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4)) return FA_ERROR_INVALID_VALUE;
+    }
+    if (q_elems > 0) {
+        if (q == nullptr || o == nullptr) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(q, 16) || !aligned(o, 16)) return FA_ERROR_INVALID_VALUE;
+        if (lse != nullptr && !aligned(lse, 4)) return FA_ERROR_INVALID_VALUE;
+    }
+    if (kv_elems > 0) {
+        if (k == nullptr || v == nullptr) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(k, 16) || !aligned(v, 16)) return FA_ERROR_INVALID_VALUE;
+    }
+    if (dtype != FA_DTYPE_BF16) return FA_ERROR_NOT_SUPPORTED;   // variable-length batches: bf16 only
+    if (d != 64 && d != 128) return FA_ERROR_NOT_SUPPORTED;
+    return FA_SUCCESS;
+}
+
+extern "C" fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs,
+                                     int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv, int d,
+                                     int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
+    const fa_status_t st = fa_fwd_varlen_validate(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, n_seqs,
+                                                  max_seqlen_q, total_q, total_k, Hq, Hkv, d, causal, scale,
+                                                  dtype);
+    if (st != FA_SUCCESS) return st;
+    if (n_seqs == 0 || max_seqlen_q == 0 || total_q == 0) return FA_SUCCESS;
+    fa::FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.B = n_seqs;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = max_seqlen_q;            // sizes the grid; each workgroup reads its sequence's length
+    p.Nk = 0;
+    p.group = Hq / Hkv;
+    p.n_heads = n_seqs * Hq;
+    p.causal_shift = 0;
+    const float mag = fabsf(scale);
+    p.c = fmaxf(mag * fa::kLog2e, FLT_MIN);
+    p.o_scale = 1.f;
+    p.q_sign = scale < 0.f ? 0x80008000u : 0u;
+    fa::VarlenParams vp{};
+    vp.cu_q = cu_seqlens_q;
+    vp.cu_k = cu_seqlens_k;
+    vp.total_q = total_q;
+    vp.total_k = total_k;
+    const hipError_t err = fa::launch_fwd_bf16_varlen(p, vp, d, causal != 0, stream);
     return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
 }
 

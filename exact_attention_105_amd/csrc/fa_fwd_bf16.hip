@@ -51,6 +51,7 @@
 
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
+#include "fa_varlen.hpp"
 
 namespace fa {
 
@@ -127,8 +128,8 @@ struct Bf16Cfg {
     static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 LDS stages");
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdParams p) {
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdParams pin, VarlenParams vp) {
     using C = Bf16Cfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
     lds_char* smem = (lds_char*)smem_raw;
@@ -140,15 +141,39 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
     const int n = lane & 31;     // query column owned by this lane (in each 32-row block)
     const int g = lane >> 5;     // which half of the 32x32 block's rows
 
-    // Workgroup -> (head, query tile), XCD-aware (tile_of in fa_device.hpp).
+    // Workgroup -> (head, query tile), XCD-aware (tile_of in fa_device.hpp);
+    // for a variable-length batch, b is the sequence.
+    FwdParams p = pin;
     int b, hq, hkv, qt;
     tile_of<CAUSAL>(p, blockIdx.x, b, hq, hkv, qt);
     const int q0 = qt * C::BM;
     const int wq0 = q0 + w * C::RW;              // first row of this wave
 
-    const char* Qh = reinterpret_cast<const char*>(p.q) + ((int64_t)(b * p.Hq + hq) * p.Nq) * C::ROW;
-    const char* Kh = reinterpret_cast<const char*>(p.k) + ((int64_t)(b * p.Hkv + hkv) * p.Nk) * C::ROW;
-    const char* Vh = reinterpret_cast<const char*>(p.v) + ((int64_t)(b * p.Hkv + hkv) * p.Nk) * C::ROW;
+    // Bytes between consecutive rows of one head: rows are contiguous in the
+    // [B, H, N, d] layout and H*d elements apart in the packed one.
+    const int64_t QSTR = VARLEN ? (int64_t)p.Hq * C::ROW : C::ROW;
+    const int64_t KVSTR = VARLEN ? (int64_t)p.Hkv * C::ROW : C::ROW;
+    int64_t q_tok0 = 0, k_tok0 = 0;              // first token of the sequence (packed layout)
+    if constexpr (VARLEN) {
+        // The sequence's bounds, clamped so malformed offsets cannot move any
+        // access outside the tensors; query tiles past its length exit here,
+        // before any barrier.
+        const int qa = min(max(vp.cu_q[b], 0), vp.total_q);
+        const int qe = min(max(vp.cu_q[b + 1], qa), vp.total_q);
+        const int ka = min(max(vp.cu_k[b], 0), vp.total_k);
+        const int ke = min(max(vp.cu_k[b + 1], ka), vp.total_k);
+        p.Nq = __builtin_amdgcn_readfirstlane(qe - qa);
+        p.Nk = __builtin_amdgcn_readfirstlane(ke - ka);
+        p.causal_shift = p.Nk - p.Nq;
+        q_tok0 = __builtin_amdgcn_readfirstlane(qa);
+        k_tok0 = __builtin_amdgcn_readfirstlane(ka);
+        if (q0 >= p.Nq) return;
+    }
+    const int64_t qhead = VARLEN ? q_tok0 * QSTR + (int64_t)hq * C::ROW : ((int64_t)(b * p.Hq + hq) * p.Nq) * C::ROW;
+    const int64_t kvhead = VARLEN ? k_tok0 * KVSTR + (int64_t)hkv * C::ROW : ((int64_t)(b * p.Hkv + hkv) * p.Nk) * C::ROW;
+    const char* Qh = reinterpret_cast<const char*>(p.q) + qhead;
+    const char* Kh = reinterpret_cast<const char*>(p.k) + kvhead;
+    const char* Vh = reinterpret_cast<const char*>(p.v) + kvhead;
 
     // Keys this workgroup needs: all of them, or (causal) up to the last
     // visible key of its last row; key tiles beyond are skipped entirely.
@@ -169,7 +194,7 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
     for (int qb = 0; qb < C::NQB; ++qb) {
         const int qrow = wq0 + 32 * qb + n;
         if (qrow < p.Nq) {
-            const char* src = Qh + (int64_t)qrow * C::ROW;
+            const char* src = Qh + (int64_t)qrow * QSTR;
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
                 u32x4 x = ldg16(src + (2 * ks + g) * 16);
@@ -190,8 +215,8 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
 #pragma unroll
     for (int t = 0; t < C::CPW; ++t) {
         const int row = (w * C::CPW + t) * C::RPC + c_row;
-        dk_off[t] = row * C::ROW + ((c_su ^ C::kswz(row)) << 4);
-        dv_off[t] = row * C::ROW + ((c_su ^ C::vswz(row)) << 4);
+        dk_off[t] = row * (uint32_t)KVSTR + ((c_su ^ C::kswz(row)) << 4);
+        dv_off[t] = row * (uint32_t)KVSTR + ((c_su ^ C::vswz(row)) << 4);
     }
     // K reads: row 32*kh + n, unit 2*ks + g, swizzled by row (kh adds 32 rows)
     uint32_t k_off[C::KS];
@@ -218,8 +243,8 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         const uint32_t kdst = smem_u32 + stage * C::STAGE + w * C::CPW * 1024;
         const uint32_t vdst = kdst + C::TILE;
         const int key0 = j * C::BN;
-        const char* kb = Kh + (int64_t)key0 * C::ROW;
-        const char* vb = Vh + (int64_t)key0 * C::ROW;
+        const char* kb = Kh + (int64_t)key0 * KVSTR;
+        const char* vb = Vh + (int64_t)key0 * KVSTR;
         if (key0 + C::BN <= p.Nk) {
 #pragma unroll
             for (int t = 0; t < C::CPW; ++t) {
@@ -232,8 +257,8 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
             for (int t = 0; t < C::CPW; ++t) {
                 const int row = (w * C::CPW + t) * C::RPC + c_row;
                 const int rc = min(row, last);
-                dma16(kb, rc * C::ROW + ((c_su ^ C::kswz(row)) << 4), kdst + t * 1024);
-                dma16(vb, rc * C::ROW + ((c_su ^ C::vswz(row)) << 4), vdst + t * 1024);
+                dma16(kb, rc * (uint32_t)KVSTR + ((c_su ^ C::kswz(row)) << 4), kdst + t * 1024);
+                dma16(vb, rc * (uint32_t)KVSTR + ((c_su ^ C::vswz(row)) << 4), vdst + t * 1024);
             }
         }
     };
@@ -396,11 +421,12 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         const int qrow = wq0 + 32 * qb + n;
         if (p.lse != nullptr && g == 0 && qrow < p.Nq) {
             const float v = lt > 0.f ? (mref[qb] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-            p.lse[(int64_t)(b * p.Hq + hq) * p.Nq + qrow] = v;
+            const int64_t li = VARLEN ? (int64_t)hq * vp.total_q + q_tok0 + qrow : (int64_t)(b * p.Hq + hq) * p.Nq + qrow;
+            p.lse[li] = v;
         }
     }
     __syncthreads();
-    char* Oh = reinterpret_cast<char*>(p.o) + ((int64_t)(b * p.Hq + hq) * p.Nq) * C::ROW;
+    char* Oh = reinterpret_cast<char*>(p.o) + qhead;
 #pragma unroll
     for (int it = 0; it < C::RW * C::UPR / 64; ++it) {
         const int f = it * 64 + lane;
@@ -410,27 +436,36 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         if (grow < p.Nq) {
             const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
                 smem + row * C::ROW + su * 16);
-            *reinterpret_cast<u32x4*>(Oh + (int64_t)grow * C::ROW + ((su ^ C::kswz(row)) << 4)) = v;
+            *reinterpret_cast<u32x4*>(Oh + (int64_t)grow * QSTR + ((su ^ C::kswz(row)) << 4)) = v;
         }
     }
 }
 
-template <int D, bool CAUSAL>
-static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
+template <int D, bool CAUSAL, bool VARLEN>
+static hipError_t launch_one(const FwdParams& p, const VarlenParams& vp, hipStream_t stream) {
     using C = Bf16Cfg<D>;
     FwdParams pp = p;
+    VarlenParams vv = vp;
     pp.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
     const long long grid = (long long)pp.n_qtiles * pp.n_heads;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    void* args[] = {&pp};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_bf16_kernel<D, CAUSAL>),
+    void* args[] = {&pp, &vv};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_bf16_kernel<D, CAUSAL, VARLEN>),
                            dim3((unsigned)grid), dim3(256), args, 0, stream);
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream) {
-    if (d == 64) return causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
-    if (d == 128) return causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+    const VarlenParams none{};
+    if (d == 64) return causal ? launch_one<64, true, false>(p, none, stream) : launch_one<64, false, false>(p, none, stream);
+    if (d == 128) return causal ? launch_one<128, true, false>(p, none, stream) : launch_one<128, false, false>(p, none, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_bf16_varlen(const FwdParams& p, const VarlenParams& vp, int d, bool causal,
+                                  hipStream_t stream) {
+    if (d == 64) return causal ? launch_one<64, true, true>(p, vp, stream) : launch_one<64, false, true>(p, vp, stream);
+    if (d == 128) return causal ? launch_one<128, true, true>(p, vp, stream) : launch_one<128, false, true>(p, vp, stream);
     return hipErrorInvalidValue;
 }
 

@@ -141,6 +141,41 @@ fa_status_t fa_rotate_quantize_validate(const void* x, fa_dtype_t x_dtype, long 
                                         const float* work);
 
 /*
+ * fa_fwd_varlen -- fa_fwd over a batch of sequences of different lengths,
+ * packed without padding, asynchronous on `stream` (bf16).
+ *
+ * Sequence s has the query tokens cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and
+ * the key/value tokens cu_seqlens_k[s] .. cu_seqlens_k[s+1]-1; each
+ * sequence is an independent attention problem with the masking, head
+ * grouping and bottom-right causal alignment of fa_fwd (page "Flash
+ * Attention", 21medien.de, key techniques: variable sequence lengths).
+ *
+ * Pointers (device memory, owned by the caller), token-major packed layout:
+ *   q, o   [total_q, Hq, d] bf16, aligned to 16 bytes
+ *   k, v   [total_k, Hkv, d] bf16, aligned to 16 bytes
+ *   lse    [Hq, total_q] fp32, or NULL
+ *   cu_seqlens_q, cu_seqlens_k   n_seqs + 1 int32 offsets each, device memory,
+ *          non-decreasing from 0 to total_q (total_k)
+ * max_seqlen_q must be at least every query length (it sizes the grid);
+ * query rows past it are not written.  The kernels clamp every offset to
+ * [0, total], so malformed offsets give wrong results, never an access out of
+ * bounds.  dtype must be FA_DTYPE_BF16 and d in {64, 128}.
+ *
+ * Returns as fa_fwd; nothing is launched on an argument error.
+ */
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs, int max_seqlen_q,
+                          int total_q, int total_k, int Hq, int Hkv, int d, int causal, float scale,
+                          fa_dtype_t dtype, hipStream_t stream);
+
+/* The argument checks of fa_fwd_varlen as a pure host function (the offsets
+ * themselves live in device memory and are not read). */
+fa_status_t fa_fwd_varlen_validate(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                                   int n_seqs, int max_seqlen_q, int total_q, int total_k, int Hq, int Hkv,
+                                   int d, int causal, float scale, fa_dtype_t dtype);
+
+/*
  * fa_bwd -- backward pass of fa_fwd (bf16), asynchronous on `stream`.
  *
  * Given the forward inputs q, k, v, the forward outputs o and lse (as

@@ -370,3 +370,35 @@ def attention_bwd(q, k, v, dout, *, causal: bool, scale: float, dtype: str = "bf
 def bwd_dq_rows(q, k, v, dout, *, causal: bool, scale: float, rows, dtype: str = "bf16"):
     """dQ of the listed rows (flat (b*Hq + h)*Nq + i) only, [n, d] float64."""
     return default().bwd_dq_rows(q, k, v, dout, causal=causal, scale=scale, rows=rows, dtype=dtype)
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool, scale: float,
+                     dtype: str = "bf16"):
+    """Attention over a packed batch of variable-length sequences, float64.
+
+    q [total_q, Hq, d], k and v [total_k, Hkv, d] (token-major); sequence s
+    owns query tokens cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and key tokens
+    cu_seqlens_k[s] .. cu_seqlens_k[s+1]-1 and is an independent attention
+    problem.  Returns O [total_q, Hq, d] and LSE [Hq, total_q]; each
+    sequence goes through ``attention`` in the [1, H, N, d] layout.
+    """
+    q, k, v = (np.ascontiguousarray(t) for t in (q, k, v))
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or len(cq) < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold n_seqs + 1 offsets")
+    total_q, Hq, d = q.shape
+    o = np.zeros((total_q, Hq, d), dtype=np.float64)
+    lse = np.full((Hq, total_q), -np.inf, dtype=np.float64)
+    for s in range(len(cq) - 1):
+        qa, qe, ka, ke = cq[s], cq[s + 1], ck[s], ck[s + 1]
+        if qe <= qa:
+            continue
+        qs = np.ascontiguousarray(q[qa:qe].transpose(1, 0, 2)[None])
+        ks = np.ascontiguousarray(k[ka:ke].transpose(1, 0, 2)[None])
+        vs = np.ascontiguousarray(v[ka:ke].transpose(1, 0, 2)[None])
+        os_, ls = attention(qs, ks, vs, causal=causal, scale=scale, dtype=dtype)
+        o[qa:qe] = os_[0].transpose(1, 0, 2)
+        lse[:, qa:qe] = ls[0]
+    return o, lse
+

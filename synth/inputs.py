@@ -207,3 +207,30 @@ def make_grad_output(B, Hq, Nq, d, seed):
     normals from PCG64(seed + 1000), rounded to bfloat16 (uint16 bits)."""
     rng = np.random.Generator(np.random.PCG64(seed + 1000))
     return f32_to_bf16_bits(normals(rng, (B, Hq, Nq, d)))
+
+
+# Variable-length (packed) workloads: per-sequence query and key lengths.
+VARLEN_WORKLOADS = {
+    # 24 causal sequences, lengths log-uniform in [128, 8192] (seed 105020), 16 heads, d 128
+    "varlen_mix": dict(n_seqs=24, lo=128, hi=8192, Hq=16, Hkv=16, d=128, causal=True, seed=105020),
+}
+
+
+def varlen_lengths(n_seqs, lo, hi, seed):
+    """Sequence lengths, log-uniform in [lo, hi], from PCG64(seed)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.floor(np.exp(rng.uniform(np.log(lo), np.log(hi + 1), size=n_seqs))).astype(np.int64).clip(lo, hi)
+
+
+def make_varlen_inputs(lens_q, lens_k, Hq, Hkv, d, seed):
+    """Packed bf16 inputs: q [sum lens_q, Hq, d], k and v [sum lens_k, Hkv, d]
+    (float32 standard normals from PCG64(seed), in that order, rounded to
+    bf16) and the int32 offsets cu_q, cu_k."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tq, tk = int(np.sum(lens_q)), int(np.sum(lens_k))
+    q = f32_to_bf16_bits(normals(rng, (tq, Hq, d)))
+    k = f32_to_bf16_bits(normals(rng, (tk, Hkv, d)))
+    v = f32_to_bf16_bits(normals(rng, (tk, Hkv, d)))
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    return {"q": q, "k": k, "v": v, "cu_q": cu_q, "cu_k": cu_k}

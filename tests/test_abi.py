@@ -174,3 +174,39 @@ def test_bwd_invalid_arguments(lib, kw):
                                 dict(dtype=_lib.FA_DTYPE_F32)])
 def test_bwd_unsupported(lib, kw):
     assert bvalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
+
+
+# ---------------------------------------------------------------- fa_fwd_varlen
+VGOOD = dict(q=4096, k=8192, v=12288, o=16384, lse=20480, cuq=24576, cuk=28672, n_seqs=3, max_seqlen_q=700,
+             total_q=1000, total_k=1200, Hq=8, Hkv=2, d=128, causal=1, scale=0.125, dtype=_lib.FA_DTYPE_BF16)
+
+
+def vvalidate(**kw):
+    a = dict(VGOOD)
+    a.update(kw)
+    return _lib.fa_fwd_varlen_validate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cuq"], a["cuk"], a["n_seqs"],
+                                       a["max_seqlen_q"], a["total_q"], a["total_k"], a["Hq"], a["Hkv"], a["d"],
+                                       a["causal"], a["scale"], a["dtype"])
+
+
+def test_varlen_valid_arguments(lib):
+    assert vvalidate() == _lib.FA_SUCCESS
+    assert vvalidate(d=64, causal=0, lse=None) == _lib.FA_SUCCESS
+    assert vvalidate(n_seqs=0, cuq=None, cuk=None) == _lib.FA_SUCCESS
+    assert vvalidate(total_k=0, k=None, v=None) == _lib.FA_SUCCESS
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_seqs=-1), dict(max_seqlen_q=-1), dict(total_q=-1), dict(total_k=-1), dict(Hq=0), dict(Hkv=3),
+    dict(d=0), dict(causal=5), dict(scale=math.inf), dict(dtype=9), dict(cuq=None), dict(cuk=None),
+    dict(cuq=24576 + 2), dict(q=None), dict(o=None), dict(k=None), dict(v=None), dict(q=4096 + 8),
+    dict(o=16384 + 2), dict(lse=20480 + 1), dict(total_q=1 << 22, Hq=8, d=128),
+    dict(max_seqlen_q=1 << 30, n_seqs=1 << 10),
+])
+def test_varlen_invalid_arguments(lib, kw):
+    assert vvalidate(**kw) == _lib.FA_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(dtype=_lib.FA_DTYPE_FP8_E4M3), dict(dtype=_lib.FA_DTYPE_F32)])
+def test_varlen_unsupported(lib, kw):
+    assert vvalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED

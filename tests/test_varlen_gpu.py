@@ -1,0 +1,103 @@
+"""GPU parity of fa_fwd_varlen (packed batches of sequences of different
+lengths) against the oracle, which runs every sequence as its own batch
+problem.  Same tolerances as the fixed-length bf16 path (gpu_util.py)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_105_amd import fwd, fwd_varlen
+from gpu_util import compare_bf16, say
+from synth.inputs import VARLEN_WORKLOADS, make_varlen_inputs, varlen_lengths
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import exact_attention_105_amd as fa
+    fa.load()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+
+def run_varlen(x, causal, scale, max_q=None):
+    q, k, v = (dev_bf16(x[n]) for n in ("q", "k", "v"))
+    cq = torch.from_numpy(x["cu_q"]).to("cuda:0")
+    ck = torch.from_numpy(x["cu_k"]).to("cuda:0")
+    lens = np.diff(x["cu_q"])
+    max_q = int(lens.max()) if max_q is None and lens.size else (max_q or 0)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=q.device)
+    lse = torch.full((q.shape[1], q.shape[0]), float("nan"), dtype=torch.float32, device=q.device)
+    o, l = fwd_varlen(q, k, v, cq, ck, max_q, causal=causal, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), l.cpu().double().numpy()
+
+
+# (query lengths, key lengths or None for the same, Hq, Hkv, d, causal)
+CASES = [
+    ([128, 1, 300, 0, 129], None, 4, 2, 128, True),
+    ([128, 1, 300, 0, 129], None, 4, 4, 64, False),
+    ([77, 256, 5], [200, 100, 5], 2, 1, 128, True),      # Nq < Nk, Nq > Nk, Nq = Nk per sequence
+    ([77, 256, 5], [200, 100, 5], 2, 2, 64, True),
+    ([500, 3, 260], [1, 700, 0], 4, 2, 128, False),       # a single key, an empty key side
+    ([1000], None, 8, 2, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}H{c[2]}/{c[3]}d{c[4]}{'c' if c[5] else ''}"
+                                             for c in CASES])
+def test_varlen_matches_oracle(case):
+    lq, lk, Hq, Hkv, d, causal = case
+    lk = lq if lk is None else lk
+    x = make_varlen_inputs(np.array(lq), np.array(lk), Hq, Hkv, d, 4242 + sum(lq))
+    scale = 1.0 / math.sqrt(d)
+    say(f"varlen {case}")
+    o, lse = run_varlen(x, causal, scale)
+    o_ref, lse_ref = oracle.attention_varlen(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], causal=causal, scale=scale)
+    compare_bf16(o, lse, o_ref, lse_ref, f"varlen {case}")
+
+
+def test_equal_lengths_match_the_batch_kernel_bit_for_bit():
+    """The packed path and the [B, H, N, d] path run the same arithmetic."""
+    n, N, Hq, Hkv, d = 3, 300, 4, 2, 128
+    x = make_varlen_inputs(np.full(n, N), np.full(n, N), Hq, Hkv, d, 77)
+    for causal in (False, True):
+        o, lse = run_varlen(x, causal, 0.09)
+        qb = dev_bf16(np.ascontiguousarray(x["q"].reshape(n, N, Hq, d).transpose(0, 2, 1, 3)))
+        kb = dev_bf16(np.ascontiguousarray(x["k"].reshape(n, N, Hkv, d).transpose(0, 2, 1, 3)))
+        vb = dev_bf16(np.ascontiguousarray(x["v"].reshape(n, N, Hkv, d).transpose(0, 2, 1, 3)))
+        ob, lb = fwd(qb, kb, vb, causal=causal, scale=0.09)
+        torch.cuda.synchronize()
+        ob = ob.float().cpu().double().numpy().transpose(0, 2, 1, 3).reshape(n * N, Hq, d)
+        lb = lb.cpu().double().numpy().transpose(1, 0, 2).reshape(Hq, n * N)
+        say(f"  equal lengths causal={causal}: max |varlen - batch| O {np.abs(o - ob).max():.1e} LSE {np.abs(lse - lb).max():.1e}")
+        assert np.array_equal(o, ob) and np.array_equal(lse, lb)
+
+
+def test_varlen_mix_workload_sampled_rows():
+    """The ragged bench workload at full size: sampled rows of every sequence
+    against the oracle on that sequence."""
+    w = VARLEN_WORKLOADS["varlen_mix"]
+    lens = varlen_lengths(w["n_seqs"], w["lo"], w["hi"], w["seed"])
+    x = make_varlen_inputs(lens, lens, w["Hq"], w["Hkv"], w["d"], w["seed"])
+    scale = 1.0 / math.sqrt(w["d"])
+    say(f"varlen_mix: {len(lens)} sequences, {int(lens.sum())} tokens")
+    o, lse = run_varlen(x, w["causal"], scale)
+    rng = np.random.default_rng(3)
+    cu = x["cu_q"]
+    for s in range(len(lens)):
+        L = int(lens[s])
+        qs = np.ascontiguousarray(x["q"][cu[s]:cu[s + 1]].transpose(1, 0, 2)[None])
+        ks = np.ascontiguousarray(x["k"][cu[s]:cu[s + 1]].transpose(1, 0, 2)[None])
+        vs = np.ascontiguousarray(x["v"][cu[s]:cu[s + 1]].transpose(1, 0, 2)[None])
+        rows = rng.choice(w["Hq"] * L, size=min(16, w["Hq"] * L), replace=False)   # flat (h, i) within the sequence
+        o_ref, lse_ref = oracle.attention(qs, ks, vs, causal=w["causal"], scale=scale, rows=rows)
+        h, i = rows // L, rows % L
+        compare_bf16(o[cu[s] + i, h], lse[h, cu[s] + i], o_ref, lse_ref, f"varlen_mix sequence {s} (len {L})")
