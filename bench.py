@@ -331,6 +331,98 @@ def load_bwd_traffic(cfg):
     return t.get("hbm_bytes_per_call") if t.get("kernel_source_hash") == bwd_source_hash() else None
 
 
+def varlen_bench(args):
+    """One fa_fwd_varlen call per step on a packed ragged workload; TFLOP/s
+    counts 4*d per visible (query, key) pair of every sequence and head, the
+    fixed-length convention (halved for causal self-attention).  The same
+    sequences padded to the longest one and run through fa_fwd are timed
+    beside it (padded_batch_ms)."""
+    import torch
+    from exact_attention_105_amd import fwd, fwd_varlen, load
+    from synth.inputs import VARLEN_WORKLOADS, make_varlen_inputs, varlen_lengths
+
+    load()
+    w = VARLEN_WORKLOADS[args.varlen]
+    lens = varlen_lengths(w["n_seqs"], w["lo"], w["hi"], w["seed"])
+    x = make_varlen_inputs(lens, lens, w["Hq"], w["Hkv"], w["d"], w["seed"])
+    dev = torch.device("cuda:0")
+    conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v = conv(x["q"]), conv(x["k"]), conv(x["v"])
+    cq = torch.from_numpy(x["cu_q"]).to(dev)
+    ck = torch.from_numpy(x["cu_k"]).to(dev)
+    maxlen = int(lens.max())
+    scale = 1.0 / math.sqrt(w["d"])
+    out = torch.empty_like(q)
+    lse = torch.empty((w["Hq"], q.shape[0]), dtype=torch.float32, device=dev)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(lambda: fwd_varlen(q, k, v, cq, ck, maxlen, causal=w["causal"], scale=scale, out=out, lse=lse),
+               args.steps, args.warmup)
+    L = lens.astype(np.float64)
+    pairs = np.sum(L * L / 2) if w["causal"] else np.sum(L * L)
+    flops = 4.0 * w["Hq"] * w["d"] * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    # the same sequences, zero-padded to the longest, through the fixed-length kernel
+    B = len(lens)
+    qp = torch.zeros((B, w["Hq"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
+    kp = torch.zeros((B, w["Hkv"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    ms_pad = timed(lambda: fwd(qp, kp, vp, causal=w["causal"], scale=scale), max(1, args.steps // 2), 1)
+    del qp, kp, vp
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = varlen_cpu_baseline(x, lens, w, scale, args.cpu_budget)
+    peak = PEAK_TFLOPS["bf16"]
+    print(json.dumps({
+        "metric": "varlen attention forward TFLOP/s on 1 MI355X", "value": tflops, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) inputs)",
+        "config": {"workload": args.varlen, "n_seqs": int(B), "total_tokens": int(L.sum()), "max_seqlen": maxlen,
+                   "Hq": w["Hq"], "Hkv": w["Hkv"], "d": w["d"], "causal": w["causal"], "flops_per_step": flops,
+                   "padded_batch_ms": ms_pad},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
+                     "traffic": None},
+        "cpu_baseline": cpu}), flush=True)
+
+
+def varlen_cpu_baseline(x, lens, w, scale, budget_s: float):
+    """The oracle on sampled (head, row) pairs of every sequence, about budget_s seconds."""
+    import oracle
+    rng = np.random.default_rng(31)
+    cu = x["cu_q"]
+    per = 4
+    while True:
+        t0 = time.perf_counter()
+        flops = 0.0
+        for s in range(len(lens)):
+            L = int(lens[s])
+            qs = np.ascontiguousarray(x["q"][cu[s]:cu[s + 1]].transpose(1, 0, 2)[None])
+            ks = np.ascontiguousarray(x["k"][cu[s]:cu[s + 1]].transpose(1, 0, 2)[None])
+            vs = np.ascontiguousarray(x["v"][cu[s]:cu[s + 1]].transpose(1, 0, 2)[None])
+            rows = rng.choice(w["Hq"] * L, size=min(per, w["Hq"] * L), replace=False)
+            oracle.attention(qs, ks, vs, causal=w["causal"], scale=scale, rows=rows)
+            i = rows % L
+            flops += float(np.sum(4.0 * w["d"] * ((i + 1) if w["causal"] else L)))
+        dt = time.perf_counter() - t0
+        if dt >= 0.3 * budget_s or per >= 4096:
+            break
+        per *= 4
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{per} sampled (head, row) pairs of each of {len(lens)} sequences ({dt:.1f} s)"}
+
+
 def bwd_source_hash() -> str:
     from exact_attention_105_amd import build as _build
     csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
@@ -382,6 +474,8 @@ def main():
                     help="instead of attention, time a bf16 n x n x n torch.matmul (vendor GEMM context)")
     ap.add_argument("--rotate", action="store_true",
                     help="instead of attention, time the Hadamard rotation + E4M3 quantisation step")
+    ap.add_argument("--varlen", default="",
+                    help="time fa_fwd_varlen on this packed workload (e.g. varlen_mix) instead")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd) on --config instead of the forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -403,6 +497,9 @@ def main():
         return
     if args.bwd:
         bwd_bench(args)
+        return
+    if args.varlen:
+        varlen_bench(args)
         return
 
     import torch
