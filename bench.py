@@ -474,6 +474,8 @@ def main():
                     help="instead of attention, time a bf16 n x n x n torch.matmul (vendor GEMM context)")
     ap.add_argument("--rotate", action="store_true",
                     help="instead of attention, time the Hadamard rotation + E4M3 quantisation step")
+    ap.add_argument("--splitkv", type=int, default=-1,
+                    help="decode shapes: run fa_fwd_splitkv with this many key splits (0: the library's default)")
     ap.add_argument("--varlen", default="",
                     help="time fa_fwd_varlen on this packed workload (e.g. varlen_mix) instead")
     ap.add_argument("--bwd", action="store_true",
@@ -519,8 +521,19 @@ def main():
     lse = torch.empty((cfg.B, cfg.Hq, cfg.Nq), dtype=torch.float32, device=dev)
     descale = x.get("descale")
 
-    def step():
-        fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, descale=descale, out=out, lse=lse)
+    if args.splitkv >= 0:
+        from exact_attention_105_amd import default_splits, fwd_splitkv
+        n_splits = args.splitkv or default_splits(cfg.B, cfg.Hq, cfg.Hkv, cfg.Nq, cfg.Nk)
+        ws = torch.empty(max(n_splits * cfg.B * cfg.Hq * cfg.Nq * (cfg.d + 1), 1), dtype=torch.float32, device=dev)
+
+        def step():
+            fwd_splitkv(q, k, v, causal=cfg.causal, scale=cfg.scale, n_splits=n_splits, workspace=ws, out=out,
+                        lse=lse)
+    else:
+        n_splits = None
+
+        def step():
+            fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, descale=descale, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -560,7 +573,7 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Nq": cfg.Nq,
                    "Nk": cfg.Nk, "d": cfg.d, "causal": cfg.causal, "flops_per_step": cfg.flops,
                    "algorithmic_bytes_per_step": cfg.algorithmic_bytes,
-                   "kernel_source_hash": kernel_source_hash(cfg)},
+                   "kernel_source_hash": kernel_source_hash(cfg), "n_splits": n_splits},
         "roofline": roof,
         "wall_s_timed": wall,
     }

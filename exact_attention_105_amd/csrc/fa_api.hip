@@ -289,3 +289,52 @@ extern "C" fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v
     return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
 }
 
+extern "C" fa_status_t fa_fwd_splitkv_validate(const void* q, const void* k, const void* v, const void* o,
+                                               const float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                               int causal, float scale, fa_dtype_t dtype, int n_splits,
+                                               const float* workspace) {
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3 && dtype != FA_DTYPE_F32)
+        return FA_ERROR_INVALID_VALUE;
+    // sizes, pointers and alignment as for fa_fwd
+    if (fa_fwd_validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, FA_DTYPE_BF16, nullptr) ==
+        FA_ERROR_INVALID_VALUE)
+        return FA_ERROR_INVALID_VALUE;
+    if (n_splits < 1 || n_splits > 256) return FA_ERROR_INVALID_VALUE;
+    const int64_t rows = (int64_t)B * Hq * Nq;
+    if (n_splits > 1 && rows > 0) {
+        if (workspace == nullptr || !aligned(workspace, 16)) return FA_ERROR_INVALID_VALUE;
+        if (rows * n_splits * (int64_t)(d + 1) > kMaxElems) return FA_ERROR_INVALID_VALUE;
+    }
+    if (dtype != FA_DTYPE_BF16) return FA_ERROR_NOT_SUPPORTED;   // split-KV decode: bf16 only
+    if (d != 128 || Nq > 16) return FA_ERROR_NOT_SUPPORTED;      // decode shapes only
+    return FA_SUCCESS;
+}
+
+extern "C" fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                      int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                                      fa_dtype_t dtype, int n_splits, float* workspace, hipStream_t stream) {
+    const fa_status_t st = fa_fwd_splitkv_validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype,
+                                                   n_splits, workspace);
+    if (st != FA_SUCCESS) return st;
+    if ((int64_t)B * Hq * Nq == 0) return FA_SUCCESS;
+    fa::FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.group = Hq / Hkv;
+    p.n_heads = B * Hq;
+    p.causal_shift = Nk - Nq;
+    p.c = fmaxf(fabsf(scale) * fa::kLog2e, FLT_MIN);
+    p.o_scale = 1.f;
+    p.q_sign = scale < 0.f ? 0x80008000u : 0u;
+    const hipError_t err = fa::launch_fwd_decode_split(p, causal != 0, n_splits, workspace, stream);
+    return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
+}
+

@@ -17,6 +17,11 @@
 //     merged at the end through LDS with the same rescaling rule (the merge
 //     step of page "FlashAttention (DE)", systems-analysis.info, section
 //     "Online-Softmax-Berechnung", applied across ranges instead of tiles).
+// Split-KV: with few (batch, key/value head) units the grid cannot fill the
+// GPU, so the keys can also be split over n_splits workgroups.  Each then
+// writes its normalised fp32 partial O and its base-2 LSE to the caller's
+// workspace, and fa_decode_merge_kernel combines the splits with the same
+// rescaling rule (O = sum_s 2^(lse_s - M) O_s / sum_s 2^(lse_s - M)).
 // Packed row r of row tile rt is query index i = (32*rt + r) / G of query
 // head hkv*G + (32*rt + r) % G.  Products, masking, softmax and LDS layouts
 // follow fa_fwd_bf16.hip (S^T = K Q^T, O^T += V^T P^T, transposing V reads).
@@ -40,7 +45,7 @@ constexpr int kCH = kTILE / 1024;      // 1 KiB copies per tile and tensor: 8
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int causal) {
+__global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int causal, int n_splits, float* ws) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[kLDS];
     lds_char* smem = (lds_char*)smem_raw;
     const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
@@ -51,10 +56,13 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int 
     const int n = lane & 31;
     const int g = lane >> 5;
 
-    // workgroup -> (row tile, batch, key/value head)
+    // workgroup -> (key split, row tile, batch, key/value head)
     const int units = p.B * p.Hkv;
     const int unit = blockIdx.x % units;
-    const int rt = blockIdx.x / units;
+    const int row_tiles = (p.Nq * p.group + 31) / 32;
+    const int tsel = blockIdx.x / units;
+    const int rt = tsel % row_tiles;
+    const int split = tsel / row_tiles;
     const int b = unit / p.Hkv;
     const int hkv = unit % p.Hkv;
     const int G = p.group;
@@ -84,11 +92,14 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int 
     // last visible key of this row (bottom-right causal), else the last key
     const int lim_row = (causal && row_ok) ? min(qi + p.causal_shift, p.Nk - 1) : p.Nk - 1;
 
-    // this wave's key range, in whole tiles
+    // this workgroup's key split and this wave's quarter of it, in whole tiles
     const int n_tiles_all = (p.Nk + kBN - 1) / kBN;
-    const int per = (n_tiles_all + kNW - 1) / kNW;
-    const int t0 = min(w * per, n_tiles_all);
-    const int t1 = min(t0 + per, n_tiles_all);
+    const int per_split = (n_tiles_all + n_splits - 1) / n_splits;
+    const int s0 = min(split * per_split, n_tiles_all);
+    const int s1 = min(s0 + per_split, n_tiles_all);
+    const int per = (s1 - s0 + kNW - 1) / kNW;
+    const int t0 = min(s0 + w * per, s1);
+    const int t1 = min(t0 + per, s1);
 
     // per-lane copy offsets: chunk c holds tile rows 4c .. 4c+3
     const int c_row = lane >> 4, c_su = lane & 15;
@@ -249,20 +260,56 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int 
             }
             const float inv = L > 0.f ? p.o_scale / L : 0.f;
             const int i = rr / G, h = hkv * G + rr % G;
-            char* orow = reinterpret_cast<char*>(p.o) + (((int64_t)(b * p.Hq + h) * p.Nq + i) * kD + d0) * 2;
-            u32x4 v0, v1;
+            const int64_t orow_idx = (int64_t)(b * p.Hq + h) * p.Nq + i;
+            if (n_splits == 1) {
+                char* orow = reinterpret_cast<char*>(p.o) + (orow_idx * kD + d0) * 2;
+                u32x4 v0, v1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v0[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
-                v1[e] = pack_bf16x2(acc[8 + 2 * e] * inv, acc[8 + 2 * e + 1] * inv);
+                for (int e = 0; e < 4; ++e) {
+                    v0[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+                    v1[e] = pack_bf16x2(acc[8 + 2 * e] * inv, acc[8 + 2 * e + 1] * inv);
+                }
+                *reinterpret_cast<u32x4*>(orow) = v0;
+                *reinterpret_cast<u32x4*>(orow + 16) = v1;
+                if (p.lse != nullptr && (tid & 7) == 0)
+                    p.lse[orow_idx] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+            } else {
+                // this split's partial: normalised fp32 O, and its base-2 LSE
+                const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+                float* op = ws + ((int64_t)split * R + orow_idx) * kD + d0;
+#pragma unroll
+                for (int e = 0; e < 16; e += 4)
+                    *reinterpret_cast<f32x4*>(op + e) =
+                        f32x4{acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+                if ((tid & 7) == 0)
+                    ws[(int64_t)n_splits * R * kD + (int64_t)split * R + orow_idx] =
+                        L > 0.f ? M + __builtin_amdgcn_logf(L) : -INFINITY;
             }
-            *reinterpret_cast<u32x4*>(orow) = v0;
-            *reinterpret_cast<u32x4*>(orow + 16) = v1;
-            if (p.lse != nullptr && (tid & 7) == 0)
-                p.lse[(int64_t)(b * p.Hq + h) * p.Nq + i] =
-                    L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
         }
     }
+}
+
+// Combine the n_splits partials of one output row (one workgroup per row,
+// one thread per column of d): weights 2^(lse_s - M), M the largest lse_s.
+__global__ __launch_bounds__(kD) void fa_decode_merge_kernel(FwdParams p, int n_splits, const float* ws) {
+    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+    const int64_t r = blockIdx.x;
+    const int t = threadIdx.x;
+    const float* lse2 = ws + (int64_t)n_splits * R * kD;
+    float M = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, lse2[(int64_t)s * R + r]);
+    float L = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < n_splits; ++s) {
+            const float ls = lse2[(int64_t)s * R + r];
+            const float a = ls == -INFINITY ? 0.f : fast_exp2(ls - M);
+            L += a;
+            acc += a * ws[((int64_t)s * R + r) * kD + t];
+        }
+    }
+    const float o = L > 0.f ? acc / L : 0.f;
+    reinterpret_cast<__bf16*>(p.o)[r * kD + t] = static_cast<__bf16>(o);
+    if (t == 0 && p.lse != nullptr) p.lse[r] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
 bool decode_applies(const FwdParams& p, int d, bool is_bf16) {
@@ -270,15 +317,27 @@ bool decode_applies(const FwdParams& p, int d, bool is_bf16) {
 }
 
 hipError_t launch_fwd_decode(const FwdParams& p, bool causal, hipStream_t stream) {
+    return launch_fwd_decode_split(p, causal, 1, nullptr, stream);
+}
+
+hipError_t launch_fwd_decode_split(const FwdParams& p, bool causal, int n_splits, float* ws, hipStream_t stream) {
     const long long row_tiles = ((long long)p.Nq * p.group + 31) / 32;
-    const long long grid = row_tiles * p.B * p.Hkv;
+    const long long grid = row_tiles * p.B * p.Hkv * n_splits;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     FwdParams pp = p;
     int c = causal ? 1 : 0;
-    void* args[] = {&pp, &c};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_decode_kernel), dim3((unsigned)grid),
-                           dim3(256), args, 0, stream);
+    int ns = n_splits;
+    float* w = ws;
+    void* args[] = {&pp, &c, &ns, &w};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_decode_kernel), dim3((unsigned)grid),
+                                   dim3(256), args, 0, stream);
+    if (e != hipSuccess || n_splits == 1) return e;
+    const long long rows = (long long)p.B * p.Hq * p.Nq;
+    if (rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    void* margs[] = {&pp, &ns, &w};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fa_decode_merge_kernel), dim3((unsigned)rows), dim3(kD),
+                           margs, 0, stream);
 }
 
 }  // namespace fa

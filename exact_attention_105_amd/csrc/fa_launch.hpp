@@ -17,6 +17,10 @@ hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t st
 // keys split over the waves of a workgroup.
 bool decode_applies(const FwdParams& p, int d, bool is_bf16);
 hipError_t launch_fwd_decode(const FwdParams& p, bool causal, hipStream_t stream);
+// The decode kernel with the keys split over n_splits workgroups: partials go
+// to ws (n_splits * B * Hq * Nq * (128 + 1) floats), then a merge kernel
+// writes O and LSE.  n_splits == 1 is the direct path (ws unused).
+hipError_t launch_fwd_decode_split(const FwdParams& p, bool causal, int n_splits, float* ws, hipStream_t stream);
 
 // Random-sign Hadamard rotation + per-tensor E4M3 quantisation of [rows, d].
 struct RotParams {

@@ -176,6 +176,35 @@ fa_status_t fa_fwd_varlen_validate(const void* q, const void* k, const void* v, 
                                    int d, int causal, float scale, fa_dtype_t dtype);
 
 /*
+ * fa_fwd_splitkv -- fa_fwd for decode shapes with the keys split over
+ * n_splits workgroups per (batch, key/value head), asynchronous on `stream`.
+ *
+ * Same result as fa_fwd (up to rounding order).  With few (batch, key/value
+ * head) units the decode kernel's grid cannot fill the GPU; splitting the
+ * keys gives every split its own workgroup, which writes a normalised
+ * partial O and its log-sum-exp to `workspace`; a merge kernel then combines
+ * the splits with the online-softmax rescaling rule (page "FlashAttention
+ * (DE)", systems-analysis.info, section "Online-Softmax-Berechnung").
+ *
+ * Arguments as fa_fwd (bf16, d = 128, Nq <= 16; other shapes return
+ * FA_ERROR_NOT_SUPPORTED), plus:
+ *   n_splits   1 .. 256; 1 is fa_fwd's decode path and ignores workspace
+ *   workspace  device memory of n_splits * B * Hq * Nq * (d + 1) floats,
+ *              aligned to 16 bytes, overwritten; calls that share it must be
+ *              ordered on one stream
+ * Returns as fa_fwd.  No device memory is allocated.
+ */
+fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                           int Hkv, int Nq, int Nk, int d, int causal, float scale, fa_dtype_t dtype,
+                           int n_splits, float* workspace, hipStream_t stream);
+
+/* The argument checks of fa_fwd_splitkv as a pure host function. */
+fa_status_t fa_fwd_splitkv_validate(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                    int causal, float scale, fa_dtype_t dtype, int n_splits,
+                                    const float* workspace);
+
+/*
  * fa_bwd -- backward pass of fa_fwd (bf16), asynchronous on `stream`.
  *
  * Given the forward inputs q, k, v, the forward outputs o and lse (as

@@ -81,6 +81,9 @@ CONFIGS = {
         Config("long16k_causal", 2, 16, 16, 16384, 16384, 128, True, "bf16", 105003),
         Config("gqa_causal", 4, 32, 8, 8192, 8192, 128, True, "bf16", 105004),
         Config("gqa_decode", 64, 32, 8, 1, 8192, 128, True, "bf16", 105014),
+        # one sequence decoding against a 64K-token cache: 8 key/value heads,
+        # far fewer than the GPU's 256 compute units unless the keys are split
+        Config("gqa_decode_b1", 1, 32, 8, 1, 65536, 128, True, "bf16", 105015),
         Config("fp8", 4, 16, 16, 8192, 8192, 128, False, "e4m3", 105005),
     ]
 }

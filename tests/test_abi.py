@@ -210,3 +210,36 @@ def test_varlen_invalid_arguments(lib, kw):
 @pytest.mark.parametrize("kw", [dict(d=96), dict(dtype=_lib.FA_DTYPE_FP8_E4M3), dict(dtype=_lib.FA_DTYPE_F32)])
 def test_varlen_unsupported(lib, kw):
     assert vvalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
+
+
+# ---------------------------------------------------------------- fa_fwd_splitkv
+SGOOD = dict(q=4096, k=8192, v=12288, o=16384, lse=20480, B=1, Hq=32, Hkv=8, Nq=1, Nk=65536, d=128, causal=1,
+             scale=0.088, dtype=_lib.FA_DTYPE_BF16, n_splits=16, ws=24576)
+
+
+def svalidate(**kw):
+    a = dict(SGOOD)
+    a.update(kw)
+    return _lib.fa_fwd_splitkv_validate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                        a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"],
+                                        a["n_splits"], a["ws"])
+
+
+def test_splitkv_valid_arguments(lib):
+    assert svalidate() == _lib.FA_SUCCESS
+    assert svalidate(n_splits=1, ws=None) == _lib.FA_SUCCESS
+    assert svalidate(Nq=16, n_splits=256) == _lib.FA_SUCCESS
+    assert svalidate(B=0, ws=None) == _lib.FA_SUCCESS
+
+
+@pytest.mark.parametrize("kw", [dict(n_splits=0), dict(n_splits=257), dict(ws=None), dict(ws=24576 + 8),
+                                dict(q=None), dict(Hkv=3), dict(dtype=11), dict(scale=math.nan),
+                                dict(B=64, Nq=16, n_splits=256)])
+def test_splitkv_invalid_arguments(lib, kw):
+    assert svalidate(**kw) == _lib.FA_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [dict(d=64), dict(Nq=17), dict(dtype=_lib.FA_DTYPE_FP8_E4M3),
+                                dict(dtype=_lib.FA_DTYPE_F32)])
+def test_splitkv_unsupported(lib, kw):
+    assert svalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
