@@ -67,10 +67,11 @@ def kernel_source_hash(cfg) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(cfg):
+def load_traffic(cfg, variant: str = ""):
     """HBM traffic per launch from the committed counter summary, if it was
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}.json")
+    taken on the current kernel sources; else None.  ``variant`` selects a
+    summary of another path over the same workload (``_splitkv``)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{cfg.name}{variant}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -562,7 +563,7 @@ def main():
         peak = PEAK_TFLOPS[cfg.dtype]
         roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": tflops / peak}
-    roof["traffic"] = load_traffic(cfg)
+    roof["traffic"] = load_traffic(cfg, "_splitkv" if n_splits else "")
     roof["kernel_ms"] = ms
 
     result = {
