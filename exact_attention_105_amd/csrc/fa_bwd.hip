@@ -40,9 +40,6 @@
 #include "fa_bwd.hpp"
 #include "fa_device.hpp"
 
-#ifndef FA_BWD_DKV_HALVES
-#define FA_BWD_DKV_HALVES 2
-#endif
 
 namespace fa {
 
@@ -53,10 +50,6 @@ struct BwdCfg {
     static constexpr int NW = 4;                  // waves per workgroup
     static constexpr int ROWS = 128;              // query rows (dQ) or keys (dK/dV) per workgroup
     static constexpr int T = 32;                  // keys per streamed tile (dQ kernel)
-    static constexpr int NH = FA_BWD_DKV_HALVES;  // 32-row query halves per tile (dK/dV kernel)
-    static constexpr int TQ = 32 * NH;            // query rows per streamed tile (dK/dV kernel)
-    static constexpr int QSTAGE = 2 * TQ * D * 2; // Q tile + dO tile
-    static constexpr int QTILES = 2 * QSTAGE;     // two stages
     static constexpr int ROW = D * 2;             // bytes per row
     static constexpr int UPR = D / 8;             // 16-byte units per row
     static constexpr int KS = D / 16;             // MFMA steps over d
@@ -64,16 +57,36 @@ struct BwdCfg {
     static constexpr int TILE = T * ROW;          // bytes of one streamed tile of one tensor
     static constexpr int STAGE = 2 * TILE;        // two tensors per stage
     static constexpr int TILES = 2 * STAGE;       // two stages
-    static constexpr int SCRATCH = 8 * TQ * NW;   // per wave: 2 * TQ floats of row statistics (dK/dV kernel)
     static constexpr int OUT = ROWS * ROW;        // epilogue staging of 128 output rows
     static constexpr int LDS = TILES > OUT ? TILES : OUT;                       // dQ kernel
-    static constexpr int LDS_KV = QTILES + SCRATCH > OUT ? QTILES + SCRATCH : OUT;   // dK/dV kernel
     static constexpr int RPC = 1024 / ROW;        // rows per 1 KiB copy
     // 16-byte-unit XOR swizzle of LDS rows: the 16 rows one ds_read_b128
     // cycle touches cover all units (row mod 16 for 256-byte rows, (row/2)
     // mod 8 for 128-byte rows, two of which share a bank sweep).  It is
     // unchanged by a step of 16 rows.
     __device__ static constexpr int swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+};
+
+// dK/dV kernel: NH 32-row query halves per streamed tile.  Two halves give
+// the MFMA pipe the second half's S and dP products while the first half's
+// exponentials run, but cost 32 more registers per half; at d = 128 the
+// non-causal kernel (which keeps more loop state) would spill with two.
+enum KvMode { kBoth = 0, kOnlyDV = 1, kOnlyDK = 2 };
+
+#ifndef FA_BWD_SPLIT_DKV
+#define FA_BWD_SPLIT_DKV 1   // d = 128: dV and dK in two kernels (fewer registers each)
+#endif
+
+template <int D, bool CAUSAL, int MODE = kBoth>
+struct KvCfg {
+    using C = BwdCfg<D>;
+    static constexpr int NH = (D == 128 && (MODE == kOnlyDK || (!CAUSAL && MODE == kBoth))) ? 1 : 2;
+    static constexpr int OCC = MODE != kBoth ? 2 : (D == 128 ? 1 : 2);   // workgroups per CU
+    static constexpr int TQ = 32 * NH;            // query rows per streamed tile
+    static constexpr int QSTAGE = 2 * TQ * D * 2; // Q tile + dO tile
+    static constexpr int QTILES = 2 * QSTAGE;     // two stages
+    static constexpr int SCRATCH = 8 * TQ * C::NW;   // per wave: 2 * TQ floats of row statistics
+    static constexpr int LDS = QTILES + SCRATCH > C::OUT ? QTILES + SCRATCH : C::OUT;
 };
 
 // Workgroup barrier without a memory fence; the tile copies are awaited with
@@ -231,11 +244,13 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- 2. dK and dV
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdParams p) {
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv_kernel(BwdParams p) {
     using C = BwdCfg<D>;
-    constexpr int NH = C::NH, TQ = C::TQ;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS_KV];
+    using K = KvCfg<D, CAUSAL, MODE>;
+    constexpr bool DO_DV = MODE != kOnlyDK, DO_DK = MODE != kOnlyDV;
+    constexpr int NH = K::NH, TQ = K::TQ;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[K::LDS];
     lds_char* smem = (lds_char*)smem_raw;
     const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
     const int tid = threadIdx.x;
@@ -256,9 +271,9 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
     const int key = wk0 + n;
 
     const int64_t kvrow0 = (int64_t)(b * p.Hkv + hkv) * p.Nk;
-    bf16x8 kf[C::KS], vf[C::KS];
+    bf16x8 kf[C::KS], vf[DO_DK ? C::KS : 1];
     load_b_rows<D>(reinterpret_cast<const char*>(p.k) + kvrow0 * C::ROW, key, p.Nk, g, kf);
-    load_b_rows<D>(reinterpret_cast<const char*>(p.v) + kvrow0 * C::ROW, key, p.Nk, g, vf);
+    if constexpr (DO_DK) load_b_rows<D>(reinterpret_cast<const char*>(p.v) + kvrow0 * C::ROW, key, p.Nk, g, vf);
 
     // query tiles to visit, per query head of the group
     const int qs = CAUSAL ? max(0, k0 - p.causal_shift) : 0;       // first query that sees key k0
@@ -269,7 +284,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
     const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
 
     const TileOffsets<D> off(n, g);
-    float* scratch = reinterpret_cast<float*>(smem_raw + C::QTILES + w * 8 * TQ);
+    float* scratch = reinterpret_cast<float*>(smem_raw + K::QTILES + w * 8 * TQ);
 
     f32x16 dk[C::DB], dv[C::DB];
 #pragma unroll
@@ -289,7 +304,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
         const int64_t qrow0 = (int64_t)(b * p.Hq + h) * p.Nq;
         copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qrow0 * C::ROW,
                          reinterpret_cast<const char*>(p.dout) + qrow0 * C::ROW, qt * TQ, p.Nq,
-                         smem_u32 + stage * C::QSTAGE, w, lane);
+                         smem_u32 + stage * K::QSTAGE, w, lane);
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
             const int r = min(qt * TQ + 32 * hh + n, p.Nq - 1);
@@ -310,7 +325,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
             if (it + 1 < n_it) issue(it + 1, STG ^ 1);
             return;
         }
-        const lds_char* qb = smem + STG * C::QSTAGE;
+        const lds_char* qb = smem + STG * K::QSTAGE;
         const lds_char* ob = qb + TQ * C::ROW;
         // S and dP of every half first: the MFMA pipe works through the later
         // halves while the first half's exponentials run on the VALU
@@ -324,7 +339,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
                 s[hh] = mfma_bf16_32x32x16(lds_b128(qb + 32 * hh * C::ROW + off.b[ks]), kf[ks], s[hh]);
-                dp[hh] = mfma_bf16_32x32x16(lds_b128(ob + 32 * hh * C::ROW + off.b[ks]), vf[ks], dp[hh]);
+                if constexpr (DO_DK)
+                    dp[hh] = mfma_bf16_32x32x16(lds_b128(ob + 32 * hh * C::ROW + off.b[ks]), vf[ks], dp[hh]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -339,7 +355,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(scratch + 32 * hh + 8 * a + 4 * g);
-                const f32x4 y = *reinterpret_cast<const f32x4*>(scratch + TQ + 32 * hh + 8 * a + 4 * g);
+                f32x4 y = f32x4{};
+                if constexpr (DO_DK) y = *reinterpret_cast<const f32x4*>(scratch + TQ + 32 * hh + 8 * a + 4 * g);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     l2[4 * a + r] = x[r];
@@ -359,8 +376,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
                 ds[i] = e * (dp[hh][i] - dl[i]);
             }
             bf16x8 pp[2], pd[2];
-            pack_b(pv, pp);
-            pack_b(ds, pd);
+            if constexpr (DO_DV) pack_b(pv, pp);
+            if constexpr (DO_DK) pack_b(ds, pd);
             const lds_char* qbh = qb + 32 * hh * C::ROW;
             const lds_char* obh = ob + 32 * hh * C::ROW;
             __builtin_amdgcn_sched_barrier(0);
@@ -369,8 +386,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
-                    dv[db] = mfma_bf16_32x32x16(tr_operand<D>(obh, off, db, st), pp[st], dv[db]);
-                    dk[db] = mfma_bf16_32x32x16(tr_operand<D>(qbh, off, db, st), pd[st], dk[db]);
+                    if constexpr (DO_DV) dv[db] = mfma_bf16_32x32x16(tr_operand<D>(obh, off, db, st), pp[st], dv[db]);
+                    if constexpr (DO_DK) dk[db] = mfma_bf16_32x32x16(tr_operand<D>(qbh, off, db, st), pd[st], dk[db]);
                 }
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(0);
@@ -385,8 +402,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void fa_bwd_dkv_kernel(BwdPa
 
     char* dK = reinterpret_cast<char*>(p.dk) + kvrow0 * C::ROW;
     char* dV = reinterpret_cast<char*>(p.dv) + kvrow0 * C::ROW;
-    store_rows<D>(smem, dk, p.scale, dK, k0, p.Nk, w, n, g, lane);
-    store_rows<D>(smem, dv, 1.f, dV, k0, p.Nk, w, n, g, lane);
+    if constexpr (DO_DK) store_rows<D>(smem, dk, p.scale, dK, k0, p.Nk, w, n, g, lane);
+    if constexpr (DO_DV) store_rows<D>(smem, dv, 1.f, dV, k0, p.Nk, w, n, g, lane);
 }
 
 // ---------------------------------------------------------------- 3. dQ
@@ -521,8 +538,16 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     const int64_t kv_grid = (int64_t)pp.n_ktiles * p.B * p.Hkv;
     if (kv_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if (kv_grid > 0) {
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL>), dim3((unsigned)kv_grid),
-                            dim3(256), args, 0, stream);
+        if constexpr (FA_BWD_SPLIT_DKV && D == 128) {
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDV>),
+                                dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
+            if (e != hipSuccess) return e;
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDK>),
+                                dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
+        } else {
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kBoth>),
+                                dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
+        }
         if (e != hipSuccess) return e;
     }
     pp.n_qtiles = (p.Nq + C::ROWS - 1) / C::ROWS;
