@@ -394,8 +394,21 @@ def varlen_bench(args):
                    "Hq": w["Hq"], "Hkv": w["Hkv"], "d": w["d"], "causal": w["causal"], "flops_per_step": flops,
                    "padded_batch_ms": ms_pad},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
-                     "traffic": None},
+                     "traffic": load_varlen_traffic(args.varlen)},
         "cpu_baseline": cpu}), flush=True)
+
+
+def load_varlen_traffic(name: str):
+    """HBM bytes per fa_fwd_varlen call from the committed counter summary, if
+    taken on the current bf16 prefill kernel source; else None."""
+    from synth.inputs import CONFIGS
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ok = t.get("kernel_source_hash") == kernel_source_hash(CONFIGS["long16k_causal"])
+    return t.get("hbm_bytes_per_launch") if ok else None
 
 
 def varlen_cpu_baseline(x, lens, w, scale, budget_s: float):
