@@ -12,6 +12,13 @@ for the kernel (MFMA-bound: achieved TFLOP/s against the dense MFMA peak of
 the input dtype; HBM-bound decode: algorithmic GB/s against 8 TB/s) and a
 ``cpu_baseline`` object: the fp64 oracle timed on this host's cores on a
 bounded sample of rows of the same workload.
+
+Other legs, each printing its own line of the same shape:
+  --splitkv N       decode shapes through fa_fwd_splitkv (N key splits, 0: default)
+  --varlen NAME     a packed variable-length workload through fa_fwd_varlen
+  --bwd             the backward pass fa_bwd on --config's shape
+  --rotate          the random-sign Hadamard rotation + E4M3 quantisation
+  --gemm-reference N, --copy-bytes N   vendor GEMM and copy-kernel context
 """
 from __future__ import annotations
 
