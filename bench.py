@@ -88,6 +88,20 @@ def load_traffic(cfg, variant: str = ""):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first /proc/cpuinfo entry) and logical CPUs."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name}, {len(os.sched_getaffinity(0))} logical CPUs available"
+
+
 def cpu_baseline(cfg, x, budget_s: float):
     """Time the oracle on sampled rows of the workload for about budget_s seconds."""
     import oracle
@@ -119,7 +133,7 @@ def cpu_baseline(cfg, x, budget_s: float):
     # the metric's FLOP convention: 4*d per visible (query, key) pair, with the
     # causal square problem counted at half the full-matrix work
     flops = 4.0 * cfg.d * float(vis.sum())
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{n} uniformly sampled query rows of {cfg.name} ({n / total_rows:.2%} of the rows, "
                       f"{flops / 1e9:.1f} GFLOP by the visible-key count) in {dt:.1f} s, fp64"}
 
@@ -256,7 +270,7 @@ def rotate_bench(args):
     cpu = None
     if args.cpu_budget > 0:
         v, threads, sample = rotate_cpu_baseline(qf.reshape(-1, cfg.d), signs, args.cpu_budget)
-        cpu = {"value": v, "unit": "GB/s", "cores": threads, "kind": "oracle", "sample": sample}
+        cpu = {"value": v, "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(), "sample": sample}
     del qf
     print(json.dumps({"metric": "rotate+quantize E4M3 GB/s (algorithmic) on 1 MI355X", "value": gbs,
                       "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -440,7 +454,7 @@ def varlen_cpu_baseline(x, lens, w, scale, budget_s: float):
         if dt >= 0.3 * budget_s or per >= 4096:
             break
         per *= 4
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{per} sampled (head, row) pairs of each of {len(lens)} sequences ({dt:.1f} s)"}
 
 
@@ -479,7 +493,7 @@ def bwd_cpu_baseline(cfg, x, dob, budget_s: float):
     i = rows % cfg.Nq
     vis = np.minimum(cfg.Nk, i + cfg.Nk - cfg.Nq + 1) if cfg.causal else np.full(n, cfg.Nk)
     flops = float(np.sum(6.0 * np.maximum(vis, 0) * cfg.d))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
             "sample": f"row-local dQ of {n} sampled query rows ({dt:.1f} s)"}
 
 
@@ -495,6 +509,8 @@ def main():
                     help="instead of attention, time a bf16 n x n x n torch.matmul (vendor GEMM context)")
     ap.add_argument("--rotate", action="store_true",
                     help="instead of attention, time the Hadamard rotation + E4M3 quantisation step")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="also time launches after overwriting this many MB of scratch (cold caches)")
     ap.add_argument("--splitkv", type=int, default=-1,
                     help="decode shapes: run fa_fwd_splitkv with this many key splits (0: the library's default)")
     ap.add_argument("--varlen", default="",
@@ -560,18 +576,38 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive launches: the first-to-last span gives the
+    # whole-job time, the gaps give per-launch median and minimum
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_total = ev0.elapsed_time(ev1)
+    ms_total = evs[0].elapsed_time(evs[-1])
     ms = ms_total / args.steps
+    per_launch = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = per_launch[len(per_launch) // 2]
+    ms_min = per_launch[0]
+    ms_flushed = None
+    if args.flush_mb > 0:
+        # cold-cache launches: overwrite a scratch buffer larger than the
+        # 256 MB memory-side cache before each timed launch
+        scratch = torch.empty(args.flush_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        cold = []
+        for _ in range(max(3, args.steps // 2)):
+            scratch.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        ms_flushed = sorted(cold)[len(cold) // 2]
+        del scratch
     tflops = cfg.flops / (ms * 1e-3) / 1e12
 
     hbm_bound = cfg.Nq == 1
@@ -585,6 +621,10 @@ def main():
                 "frac": tflops / peak}
     roof["traffic"] = load_traffic(cfg, "_splitkv" if n_splits else "")
     roof["kernel_ms"] = ms
+    roof["kernel_ms_median"] = ms_median
+    roof["kernel_ms_min"] = ms_min
+    if ms_flushed is not None:
+        roof["kernel_ms_flushed_median"] = ms_flushed
 
     result = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
