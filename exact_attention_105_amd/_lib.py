@@ -23,8 +23,8 @@ FA_ERROR_LAUNCH_FAILURE = 3
 
 # every symbol include/fa.h declares
 EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_fwd_varlen", "fa_fwd_varlen_validate", "fa_fwd_splitkv",
-            "fa_fwd_splitkv_validate", "fa_bwd", "fa_bwd_validate", "fa_rotate_quantize_e4m3",
-            "fa_rotate_quantize_validate", "fa_status_string", "fa_version")
+            "fa_fwd_splitkv_validate", "fa_bwd", "fa_bwd_validate", "fa_bwd_varlen", "fa_bwd_varlen_validate",
+            "fa_rotate_quantize_e4m3", "fa_rotate_quantize_validate", "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -67,6 +67,10 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd.argtypes = [vp] * 10 + [i32] * 7 + [f32, i32, vp]
     lib.fa_bwd_validate.restype = i32
     lib.fa_bwd_validate.argtypes = [vp] * 10 + [i32] * 7 + [f32, i32]
+    lib.fa_bwd_varlen.restype = i32
+    lib.fa_bwd_varlen.argtypes = [vp] * 12 + [i32] * 9 + [f32, i32, vp]
+    lib.fa_bwd_varlen_validate.restype = i32
+    lib.fa_bwd_varlen_validate.argtypes = [vp] * 12 + [i32] * 9 + [f32, i32]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [i32]
     lib.fa_version.restype = i32
@@ -143,6 +147,24 @@ def fa_bwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
     """Raw call of fa_bwd_validate (pure host function); returns the status code."""
     return load().fa_bwd_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr,
                                   B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale), int(dtype))
+
+
+def fa_bwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr, cuq_ptr, cuk_ptr,
+                  n_seqs, max_seqlen_q, max_seqlen_k, total_q, total_k, Hq, Hkv, d, causal, scale, dtype,
+                  stream) -> int:
+    """Raw call of fa_bwd_varlen with integer device pointers; returns the status code."""
+    return load().fa_bwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr,
+                                cuq_ptr, cuk_ptr, n_seqs, max_seqlen_q, max_seqlen_k, total_q, total_k, Hq, Hkv, d,
+                                int(causal), float(scale), int(dtype), stream)
+
+
+def fa_bwd_varlen_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr, cuq_ptr,
+                           cuk_ptr, n_seqs, max_seqlen_q, max_seqlen_k, total_q, total_k, Hq, Hkv, d, causal,
+                           scale, dtype) -> int:
+    """Raw call of fa_bwd_varlen_validate (pure host function)."""
+    return load().fa_bwd_varlen_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr,
+                                         ws_ptr, cuq_ptr, cuk_ptr, n_seqs, max_seqlen_q, max_seqlen_k, total_q,
+                                         total_k, Hq, Hkv, d, int(causal), float(scale), int(dtype))
 
 
 def _sign_bits_arg(sign_bits):

@@ -204,6 +204,60 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     return dq, dk, dv
 
 
+def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+               dout: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+               max_seqlen_k: int, *, causal: bool = False, scale: float | None = None,
+               dq: torch.Tensor | None = None, dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None):
+    """Backward of ``fwd_varlen``: returns (dQ, dK, dV) in the packed layouts.
+
+    o and lse [Hq, total_q] are what ``fwd_varlen`` returned; dout is the
+    gradient of the loss with respect to o.  ``workspace`` holds
+    2*Hq*total_q floats.  Runs on torch's current stream.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not t.is_cuda or t.dim() != 3 or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 [tokens, H, d] GPU tensor")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda or t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU vector")
+    n_seqs = cu_seqlens_q.numel() - 1
+    if n_seqs < 0 or cu_seqlens_k.numel() != n_seqs + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold n_seqs + 1 offsets")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk_ = k.shape
+    if dk_ != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    def out_like(t, ref, name):
+        if t is None:
+            return torch.empty(ref.shape, dtype=torch.bfloat16, device=ref.device)
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(ref.shape) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor shaped like {tuple(ref.shape)}")
+        return t
+
+    dq, dk, dv = out_like(dq, q, "dq"), out_like(dk, k, "dk"), out_like(dv, v, "dv")
+    if workspace is None:
+        workspace = torch.empty(max(2 * Hq * total_q, 1), dtype=torch.float32, device=q.device)
+    elif workspace.dtype != torch.float32 or workspace.numel() < 2 * Hq * total_q:
+        raise ValueError("workspace must hold 2*Hq*total_q float32 values")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), n_seqs, int(max_seqlen_q),
+                            int(max_seqlen_k), total_q, total_k, Hq, Hkv, d, int(bool(causal)), scale,
+                            _lib.FA_DTYPE_BF16, stream)
+    if st != _lib.FA_SUCCESS:
+        raise _lib.FaError(st, _lib.status_string(st))
+    return dq, dk, dv
+
+
 def sign_bits(signs) -> list:
     """Pack a length-d sequence of +-1 (or booleans, True = negate) into the
     d/32 words fa_rotate_quantize_e4m3 takes."""

@@ -338,3 +338,84 @@ extern "C" fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* 
     return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
 }
 
+extern "C" fa_status_t fa_bwd_varlen_validate(const void* q, const void* k, const void* v, const void* o,
+                                              const float* lse, const void* dout, const void* dq, const void* dk,
+                                              const void* dv, const float* workspace, const int* cu_seqlens_q,
+                                              const int* cu_seqlens_k, int n_seqs, int max_seqlen_q,
+                                              int max_seqlen_k, int total_q, int total_k, int Hq, int Hkv, int d,
+                                              int causal, float scale, fa_dtype_t dtype) {
+    if (n_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0 || Hq < 1 || Hkv < 1 ||
+        d < 1)
+        return FA_ERROR_INVALID_VALUE;
+    if (Hq % Hkv != 0) return FA_ERROR_INVALID_VALUE;
+    if (causal != 0 && causal != 1) return FA_ERROR_INVALID_VALUE;
+    if (!isfinite(scale)) return FA_ERROR_INVALID_VALUE;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3 && dtype != FA_DTYPE_F32)
+        return FA_ERROR_INVALID_VALUE;
+    const int64_t q_elems = (int64_t)total_q * Hq * d;
+    const int64_t kv_elems = (int64_t)total_k * Hkv * d;
+    if (q_elems > kMaxElems || kv_elems > kMaxElems) return FA_ERROR_INVALID_VALUE;
+    if ((int64_t)((max_seqlen_q + 127) / 128) * n_seqs * Hq > 0x7FFFFFFFLL ||
+        (int64_t)((max_seqlen_k + 127) / 128) * n_seqs * Hkv > 0x7FFFFFFFLL)
+        return FA_ERROR_INVALID_VALUE;
+    if (n_seqs > 0) {
+        if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4)) return FA_ERROR_INVALID_VALUE;
+    }
+    if (q_elems > 0) {
+        if (q == nullptr || o == nullptr || dout == nullptr || dq == nullptr || lse == nullptr ||
+            workspace == nullptr)
+            return FA_ERROR_INVALID_VALUE;
+        if (!aligned(q, 16) || !aligned(o, 16) || !aligned(dout, 16) || !aligned(dq, 16) ||
+            !aligned(lse, 4) || !aligned(workspace, 4))
+            return FA_ERROR_INVALID_VALUE;
+    }
+    if (kv_elems > 0) {
+        if (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr) return FA_ERROR_INVALID_VALUE;
+        if (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+            return FA_ERROR_INVALID_VALUE;
+    }
+    if (dtype != FA_DTYPE_BF16) return FA_ERROR_NOT_SUPPORTED;
+    if (d != 64 && d != 128) return FA_ERROR_NOT_SUPPORTED;
+    return FA_SUCCESS;
+}
+
+extern "C" fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                     float* workspace, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                                     int n_seqs, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                                     int Hq, int Hkv, int d, int causal, float scale, fa_dtype_t dtype,
+                                     hipStream_t stream) {
+    const fa_status_t st = fa_bwd_varlen_validate(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens_q,
+                                                  cu_seqlens_k, n_seqs, max_seqlen_q, max_seqlen_k, total_q,
+                                                  total_k, Hq, Hkv, d, causal, scale, dtype);
+    if (st != FA_SUCCESS) return st;
+    if (n_seqs == 0) return FA_SUCCESS;
+    fa::BwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.ws = workspace;
+    p.B = n_seqs;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = max_seqlen_q;       // size the grids; each workgroup reads its sequence's lengths
+    p.Nk = max_seqlen_k;
+    p.group = Hq / Hkv;
+    p.causal_shift = 0;
+    p.c = scale * fa::kLog2e;
+    p.scale = scale;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    const hipError_t err = fa::launch_bwd_varlen(p, d, causal != 0, stream);
+    return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
+}
+

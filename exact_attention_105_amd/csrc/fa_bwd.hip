@@ -99,25 +99,26 @@ __device__ __forceinline__ void bwd_barrier() {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Copy rows r0 .. r0+NR-1 of two [N, D] tensors (same layout, rows past
-// N - 1 clamped to the last row) into an LDS stage: tensor a at dst, tensor b
-// at dst + NR rows.  Every wave copies its share of the 1 KiB pieces of each.
+// Copy rows r0 .. r0+NR-1 of two tensors of D-element rows `stride` bytes
+// apart (same layout, rows past N - 1 clamped to the last row) into an LDS
+// stage: tensor a at dst, tensor b at dst + NR rows.  Every wave copies its
+// share of the 1 KiB pieces of each.
 template <int D, int NR>
 __device__ __forceinline__ void copy_pair(const char* a, const char* b, int r0, int N, uint32_t dst,
-                                          int w, int lane) {
+                                          int w, int lane, int64_t stride) {
     using C = BwdCfg<D>;
     constexpr int BYTES = NR * C::ROW;
     constexpr int PW = BYTES / 1024 / C::NW;      // pieces per wave and tensor
     static_assert(PW >= 1, "a tile must give every wave a copy");
     const int c_row = lane / C::UPR, c_su = lane % C::UPR;
-    const char* abase = a + (int64_t)r0 * C::ROW;
-    const char* bbase = b + (int64_t)r0 * C::ROW;
+    const char* abase = a + (int64_t)r0 * stride;
+    const char* bbase = b + (int64_t)r0 * stride;
     const int last = N - 1 - r0;
 #pragma unroll
     for (int t = 0; t < PW; ++t) {
         const int piece = w * PW + t;
         const int row = piece * C::RPC + c_row;
-        const uint32_t off = min(row, last) * C::ROW + ((c_su ^ C::swz(row)) << 4);
+        const uint32_t off = min(row, last) * (uint32_t)stride + ((c_su ^ C::swz(row)) << 4);
         dma16(abase, off, dst + piece * 1024);
         dma16(bbase, off, dst + BYTES + piece * 1024);
     }
@@ -164,12 +165,14 @@ __device__ __forceinline__ void pack_b(const f32x16& v, bf16x8 (&out)[2]) {
     }
 }
 
-// Row `row` of a [*, D] bf16 tensor as B operands (zeros past the end).
+// Row `row` of a bf16 tensor with rows `stride` bytes apart as B operands
+// (zeros past the end).
 template <int D>
-__device__ __forceinline__ void load_b_rows(const char* base, int row, int N, int g, bf16x8 (&f)[D / 16]) {
+__device__ __forceinline__ void load_b_rows(const char* base, int row, int N, int g, bf16x8 (&f)[D / 16],
+                                            int64_t stride) {
     using C = BwdCfg<D>;
     if (row < N) {
-        const char* src = base + (int64_t)row * C::ROW;
+        const char* src = base + (int64_t)row * stride;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) f[ks] = __builtin_bit_cast(bf16x8, ldg16(src + (2 * ks + g) * 16));
     } else {
@@ -180,10 +183,11 @@ __device__ __forceinline__ void load_b_rows(const char* base, int row, int N, in
 
 // Scale 128 rows of fp32 accumulators (X^T blocks per wave: lane = row
 // 32*w + n, d = 32*db + 8*i4 + 4*g + r), convert to bf16, stage them in LDS
-// and write whole rows to dst with 16-byte coalesced stores.
+// and write whole rows (`stride` bytes apart) to dst with 16-byte coalesced
+// stores.
 template <int D>
 __device__ __forceinline__ void store_rows(lds_char* smem, const f32x16 (&acc)[D / 32], float mul, char* dst,
-                                           int r0, int N, int w, int n, int g, int lane) {
+                                           int r0, int N, int w, int n, int g, int lane, int64_t stride) {
     using C = BwdCfg<D>;
     __syncthreads();
     const int row = w * 32 + n;
@@ -207,18 +211,35 @@ __device__ __forceinline__ void store_rows(lds_char* smem, const f32x16 (&acc)[D
         const int grow = r0 + r;
         if (grow < N) {
             const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(smem + r * C::ROW + su * 16);
-            *reinterpret_cast<u32x4*>(dst + (int64_t)grow * C::ROW + ((su ^ C::swz(r)) << 4)) = v;
+            *reinterpret_cast<u32x4*>(dst + (int64_t)grow * stride + ((su ^ C::swz(r)) << 4)) = v;
         }
     }
 }
 
+// Variable-length batches: the query and key token ranges of sequence s,
+// clamped to the tensors, so malformed offsets cannot move an access out of
+// bounds.  Sets p.Nq, p.Nk and the causal shift to the sequence's own.
+__device__ __forceinline__ void seq_bounds(BwdParams& p, int s, int64_t& q_tok0, int64_t& k_tok0) {
+    const int qa = min(max(p.cu_q[s], 0), p.total_q);
+    const int qe = min(max(p.cu_q[s + 1], qa), p.total_q);
+    const int ka = min(max(p.cu_k[s], 0), p.total_k);
+    const int ke = min(max(p.cu_k[s + 1], ka), p.total_k);
+    p.Nq = __builtin_amdgcn_readfirstlane(qe - qa);
+    p.Nk = __builtin_amdgcn_readfirstlane(ke - ka);
+    p.causal_shift = p.Nk - p.Nq;
+    q_tok0 = __builtin_amdgcn_readfirstlane(qa);
+    k_tok0 = __builtin_amdgcn_readfirstlane(ka);
+}
+
 // ---------------------------------------------------------------- 1. D and base-2 LSE
 
-template <int D>
+// Rows are taken in memory order; in the packed layout row r is token r / Hq
+// of head r % Hq, whose workspace and lse index is head * total_q + token.
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
     constexpr int LPR = D / 8;          // lanes per row, 16 bytes each
     constexpr int RPW = 64 / LPR;       // rows per wave per step
-    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+    const int64_t R = VARLEN ? (int64_t)p.total_q * p.Hq : (int64_t)p.B * p.Hq * p.Nq;
     const int lane = threadIdx.x & 63;
     const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
     const int64_t n_waves = ((int64_t)gridDim.x * 256) >> 6;
@@ -235,17 +256,23 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
         if (part == 0 && r < R) {
-            p.ws[r] = acc;
-            const float l = p.lse[r];
-            p.ws[R + r] = l == -INFINITY ? INFINITY : l * kLog2e;
+            int64_t wi = r;
+            if constexpr (VARLEN) {
+                const int64_t t = r / p.Hq;
+                wi = (r - t * p.Hq) * p.total_q + t;
+            }
+            p.ws[wi] = acc;
+            const float l = p.lse[wi];
+            p.ws[R + wi] = l == -INFINITY ? INFINITY : l * kLog2e;
         }
     }
 }
 
 // ---------------------------------------------------------------- 2. dK and dV
 
-template <int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv_kernel(BwdParams p) {
+template <int D, bool CAUSAL, int MODE, bool VARLEN>
+__global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv_kernel(BwdParams pin) {
+    BwdParams p = pin;
     using C = BwdCfg<D>;
     using K = KvCfg<D, CAUSAL, MODE>;
     constexpr bool DO_DV = MODE != kOnlyDK, DO_DK = MODE != kOnlyDV;
@@ -270,10 +297,19 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
     const int wk0 = k0 + 32 * w;
     const int key = wk0 + n;
 
-    const int64_t kvrow0 = (int64_t)(b * p.Hkv + hkv) * p.Nk;
+    // bytes between consecutive rows of one head (packed layout: H*d elements)
+    const int64_t QSTR = VARLEN ? (int64_t)p.Hq * C::ROW : C::ROW;
+    const int64_t KVSTR = VARLEN ? (int64_t)p.Hkv * C::ROW : C::ROW;
+    int64_t q_tok0 = 0, k_tok0 = 0;
+    if constexpr (VARLEN) {
+        seq_bounds(p, b, q_tok0, k_tok0);
+        if (k0 >= p.Nk) return;                  // past this sequence's keys: nothing to write
+    }
+    const int64_t kvbase = VARLEN ? k_tok0 * KVSTR + (int64_t)hkv * C::ROW
+                                  : (int64_t)(b * p.Hkv + hkv) * p.Nk * C::ROW;
     bf16x8 kf[C::KS], vf[DO_DK ? C::KS : 1];
-    load_b_rows<D>(reinterpret_cast<const char*>(p.k) + kvrow0 * C::ROW, key, p.Nk, g, kf);
-    if constexpr (DO_DK) load_b_rows<D>(reinterpret_cast<const char*>(p.v) + kvrow0 * C::ROW, key, p.Nk, g, vf);
+    load_b_rows<D>(reinterpret_cast<const char*>(p.k) + kvbase, key, p.Nk, g, kf, KVSTR);
+    if constexpr (DO_DK) load_b_rows<D>(reinterpret_cast<const char*>(p.v) + kvbase, key, p.Nk, g, vf, KVSTR);
 
     // query tiles to visit, per query head of the group
     const int qs = CAUSAL ? max(0, k0 - p.causal_shift) : 0;       // first query that sees key k0
@@ -281,7 +317,7 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
     const int nqt = qs < p.Nq ? (p.Nq + TQ - 1) / TQ - qt0 : 0;
     const int n_it = __builtin_amdgcn_readfirstlane(nqt * p.group);
     const int wqs = __builtin_amdgcn_readfirstlane(CAUSAL ? max(0, wk0 - p.causal_shift) : 0);
-    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+    const int64_t R = VARLEN ? (int64_t)p.Hq * p.total_q : (int64_t)p.B * p.Hq * p.Nq;
 
     const TileOffsets<D> off(n, g);
     float* scratch = reinterpret_cast<float*>(smem_raw + K::QTILES + w * 8 * TQ);
@@ -301,14 +337,16 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
         const int gi = it / nqt;
         const int qt = qt0 + (it - gi * nqt);
         const int h = hkv * p.group + gi;
-        const int64_t qrow0 = (int64_t)(b * p.Hq + h) * p.Nq;
-        copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qrow0 * C::ROW,
-                         reinterpret_cast<const char*>(p.dout) + qrow0 * C::ROW, qt * TQ, p.Nq,
-                         smem_u32 + stage * K::QSTAGE, w, lane);
+        // first row of head h: bytes into q / dO, and its index into the workspace
+        const int64_t qbase = VARLEN ? q_tok0 * QSTR + (int64_t)h * C::ROW : (int64_t)(b * p.Hq + h) * p.Nq * C::ROW;
+        const int64_t wrow0 = VARLEN ? (int64_t)h * p.total_q + q_tok0 : (int64_t)(b * p.Hq + h) * p.Nq;
+        copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qbase,
+                         reinterpret_cast<const char*>(p.dout) + qbase, qt * TQ, p.Nq,
+                         smem_u32 + stage * K::QSTAGE, w, lane, QSTR);
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
             const int r = min(qt * TQ + 32 * hh + n, p.Nq - 1);
-            pre[hh] = p.ws[(g ? 0 : R) + qrow0 + r];
+            pre[hh] = p.ws[(g ? 0 : R) + wrow0 + r];
         }
     };
 
@@ -400,16 +438,17 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
         if (it + 1 < n_it) tile(std::integral_constant<int, 1>{}, it + 1);
     }
 
-    char* dK = reinterpret_cast<char*>(p.dk) + kvrow0 * C::ROW;
-    char* dV = reinterpret_cast<char*>(p.dv) + kvrow0 * C::ROW;
-    if constexpr (DO_DK) store_rows<D>(smem, dk, p.scale, dK, k0, p.Nk, w, n, g, lane);
-    if constexpr (DO_DV) store_rows<D>(smem, dv, 1.f, dV, k0, p.Nk, w, n, g, lane);
+    char* dK = reinterpret_cast<char*>(p.dk) + kvbase;
+    char* dV = reinterpret_cast<char*>(p.dv) + kvbase;
+    if constexpr (DO_DK) store_rows<D>(smem, dk, p.scale, dK, k0, p.Nk, w, n, g, lane, KVSTR);
+    if constexpr (DO_DV) store_rows<D>(smem, dv, 1.f, dV, k0, p.Nk, w, n, g, lane, KVSTR);
 }
 
 // ---------------------------------------------------------------- 3. dQ
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams pin) {
+    BwdParams p = pin;
     using C = BwdCfg<D>;
     __shared__ __attribute__((aligned(1024))) char smem_raw[C::LDS];
     lds_char* smem = (lds_char*)smem_raw;
@@ -436,10 +475,20 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
     const int wq0 = q0 + 32 * w;
     const int qrow = wq0 + n;
 
-    const int64_t qrow0 = (int64_t)(b * p.Hq + hq) * p.Nq;
-    const int64_t kvrow0 = (int64_t)(b * p.Hkv + hkv) * p.Nk;
-    const char* Kh = reinterpret_cast<const char*>(p.k) + kvrow0 * C::ROW;
-    const char* Vh = reinterpret_cast<const char*>(p.v) + kvrow0 * C::ROW;
+    const int64_t QSTR = VARLEN ? (int64_t)p.Hq * C::ROW : C::ROW;
+    const int64_t KVSTR = VARLEN ? (int64_t)p.Hkv * C::ROW : C::ROW;
+    int64_t q_tok0 = 0, k_tok0 = 0;
+    if constexpr (VARLEN) {
+        seq_bounds(p, b, q_tok0, k_tok0);
+        if (q0 >= p.Nq) return;                  // past this sequence's queries
+    }
+    // first row of this head: bytes into q / dO / dq and K / V, and its workspace index
+    const int64_t qbase = VARLEN ? q_tok0 * QSTR + (int64_t)hq * C::ROW : (int64_t)(b * p.Hq + hq) * p.Nq * C::ROW;
+    const int64_t kvbase = VARLEN ? k_tok0 * KVSTR + (int64_t)hkv * C::ROW
+                                  : (int64_t)(b * p.Hkv + hkv) * p.Nk * C::ROW;
+    const int64_t wrow0 = VARLEN ? (int64_t)hq * p.total_q + q_tok0 : (int64_t)(b * p.Hq + hq) * p.Nq;
+    const char* Kh = reinterpret_cast<const char*>(p.k) + kvbase;
+    const char* Vh = reinterpret_cast<const char*>(p.v) + kvbase;
 
     int kend = p.Nk;
     if (CAUSAL) kend = min(kend, max(q0 + C::ROWS + p.causal_shift, 0));
@@ -449,13 +498,13 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
     wkend = __builtin_amdgcn_readfirstlane(wkend);
 
     bf16x8 qf[C::KS], df[C::KS];
-    load_b_rows<D>(reinterpret_cast<const char*>(p.q) + qrow0 * C::ROW, qrow, p.Nq, g, qf);
-    load_b_rows<D>(reinterpret_cast<const char*>(p.dout) + qrow0 * C::ROW, qrow, p.Nq, g, df);
-    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+    load_b_rows<D>(reinterpret_cast<const char*>(p.q) + qbase, qrow, p.Nq, g, qf, QSTR);
+    load_b_rows<D>(reinterpret_cast<const char*>(p.dout) + qbase, qrow, p.Nq, g, df, QSTR);
+    const int64_t R = VARLEN ? (int64_t)p.Hq * p.total_q : (int64_t)p.B * p.Hq * p.Nq;
     float lse2 = INFINITY, dlt = 0.f;
     if (qrow < p.Nq) {
-        dlt = p.ws[qrow0 + qrow];
-        lse2 = p.ws[R + qrow0 + qrow];
+        dlt = p.ws[wrow0 + qrow];
+        lse2 = p.ws[R + wrow0 + qrow];
     }
 
     const TileOffsets<D> off(n, g);
@@ -464,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
     auto issue = [&](int j, int stage) {
-        copy_pair<D, C::T>(Kh, Vh, j * C::T, p.Nk, smem_u32 + stage * C::STAGE, w, lane);
+        copy_pair<D, C::T>(Kh, Vh, j * C::T, p.Nk, smem_u32 + stage * C::STAGE, w, lane, KVSTR);
     };
 
     auto tile = [&](auto stage_c, int j) {
@@ -517,35 +566,37 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
         if (j + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, j + 1);
     }
 
-    store_rows<D>(smem, acc, p.scale, reinterpret_cast<char*>(p.dq) + qrow0 * C::ROW, q0, p.Nq, w, n, g, lane);
+    store_rows<D>(smem, acc, p.scale, reinterpret_cast<char*>(p.dq) + qbase, q0, p.Nq, w, n, g, lane, QSTR);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     using C = BwdCfg<D>;
     BwdParams pp = p;
-    const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
+    const int64_t R = VARLEN ? (int64_t)p.total_q * p.Hq : (int64_t)p.B * p.Hq * p.Nq;
     void* args[] = {&pp};
     hipError_t e = hipSuccess;
     if (R > 0) {
         const int64_t rows_per_block = 4 * (64 / (D / 8));
         const int64_t blocks = std::min<int64_t>((R + rows_per_block - 1) / rows_per_block, 4096);
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_prep_kernel<D>), dim3((unsigned)blocks),
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_prep_kernel<D, VARLEN>), dim3((unsigned)blocks),
                             dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
     }
+    // grids: Nk / Nq are the (largest) lengths; packed workgroups past their
+    // sequence's end return at once
     pp.n_ktiles = (p.Nk + C::ROWS - 1) / C::ROWS;
     const int64_t kv_grid = (int64_t)pp.n_ktiles * p.B * p.Hkv;
     if (kv_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if (kv_grid > 0) {
         if constexpr (FA_BWD_SPLIT_DKV && D == 128) {
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDV>),
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDV, VARLEN>),
                                 dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
             if (e != hipSuccess) return e;
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDK>),
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDK, VARLEN>),
                                 dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
         } else {
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kBoth>),
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kBoth, VARLEN>),
                                 dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
         }
         if (e != hipSuccess) return e;
@@ -554,16 +605,22 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     const int64_t q_grid = (int64_t)pp.n_qtiles * p.B * p.Hq;
     if (q_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if (q_grid > 0)
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)q_grid),
-                            dim3(256), args, 0, stream);
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, VARLEN>),
+                            dim3((unsigned)q_grid), dim3(256), args, 0, stream);
     return e;
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream) {
-    if (d == 64) return causal ? launch_bwd_d<64, true>(p, stream) : launch_bwd_d<64, false>(p, stream);
-    if (d == 128) return causal ? launch_bwd_d<128, true>(p, stream) : launch_bwd_d<128, false>(p, stream);
+    if (d == 64) return causal ? launch_bwd_d<64, true, false>(p, stream) : launch_bwd_d<64, false, false>(p, stream);
+    if (d == 128) return causal ? launch_bwd_d<128, true, false>(p, stream) : launch_bwd_d<128, false, false>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_varlen(const BwdParams& p, int d, bool causal, hipStream_t stream) {
+    if (d == 64) return causal ? launch_bwd_d<64, true, true>(p, stream) : launch_bwd_d<64, false, true>(p, stream);
+    if (d == 128) return causal ? launch_bwd_d<128, true, true>(p, stream) : launch_bwd_d<128, false, true>(p, stream);
     return hipErrorInvalidValue;
 }
 

@@ -24,8 +24,16 @@ struct BwdParams {
     int n_ktiles;        // dK/dV kernel: key tiles per key/value head
     float c;             // scale * log2(e), signed
     float scale;         // multiplies dQ and dK
+    // Variable-length batches (packed [tokens, H, d] layouts): B counts
+    // sequences, Nq / Nk are the largest lengths (they size the grids), the
+    // workspace is [2][Hq][total_q] and lse is [Hq, total_q].
+    const int* cu_q;     // n_seqs + 1 offsets (device), or null
+    const int* cu_k;
+    int total_q;
+    int total_k;
 };
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_varlen(const BwdParams& p, int d, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -245,6 +245,34 @@ fa_status_t fa_bwd_validate(const void* q, const void* k, const void* v, const v
                             const void* dv, const float* workspace, int B, int Hq, int Hkv, int Nq,
                             int Nk, int d, int causal, float scale, fa_dtype_t dtype);
 
+/*
+ * fa_bwd_varlen -- fa_bwd for the packed variable-length layout of
+ * fa_fwd_varlen, asynchronous on `stream` (bf16).
+ *
+ * q, o, dout, dq [total_q, Hq, d]; k, v, dk, dv [total_k, Hkv, d]; lse
+ * [Hq, total_q] as written by fa_fwd_varlen; cu_seqlens_q / cu_seqlens_k
+ * the same device offsets (n_seqs + 1 each); max_seqlen_q / max_seqlen_k at
+ * least every query / key length (they size the grids).  workspace:
+ * 2 * Hq * total_q floats, overwritten.  Every sequence is an independent
+ * problem; the gradients are those of fa_bwd for each sequence.  dk and dv
+ * are written for every key of every sequence (zero where no query sees the
+ * key); rows past the max lengths are not written.  Offsets are clamped to
+ * [0, total] in the kernels.  Returns as fa_bwd.
+ */
+fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, float* workspace,
+                          const int* cu_seqlens_q, const int* cu_seqlens_k, int n_seqs, int max_seqlen_q,
+                          int max_seqlen_k, int total_q, int total_k, int Hq, int Hkv, int d, int causal,
+                          float scale, fa_dtype_t dtype, hipStream_t stream);
+
+/* The argument checks of fa_bwd_varlen as a pure host function. */
+fa_status_t fa_bwd_varlen_validate(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dout, const void* dq, const void* dk,
+                                   const void* dv, const float* workspace, const int* cu_seqlens_q,
+                                   const int* cu_seqlens_k, int n_seqs, int max_seqlen_q, int max_seqlen_k,
+                                   int total_q, int total_k, int Hq, int Hkv, int d, int causal, float scale,
+                                   fa_dtype_t dtype);
+
 /* A static, human-readable description of a status code. */
 const char* fa_status_string(fa_status_t status);
 

@@ -14,6 +14,6 @@ finite differences, library cross-checks).  The GPU-versus-oracle tolerances
 themselves come from the project's stated acceptance bounds (forward) and
 from the arithmetic of the kernels (backward, rotation), not from the pages.
 """
-from .oracle import (OracleLib, attention, attention_bwd, attention_varlen, build, bwd_dq_rows,  # noqa: F401
-                     decode, default, e4m3_encode, encode_scaled, hadamard_entry, num_threads, probs_row,
-                     quantize_e4m3, rotate, sign_bits)
+from .oracle import (OracleLib, attention, attention_bwd, attention_bwd_varlen, attention_varlen,  # noqa: F401
+                     build, bwd_dq_rows, decode, default, e4m3_encode, encode_scaled, hadamard_entry,
+                     num_threads, probs_row, quantize_e4m3, rotate, sign_bits)

@@ -402,3 +402,29 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool, scale
         lse[:, qa:qe] = ls[0]
     return o, lse
 
+
+def attention_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, *, causal: bool, scale: float,
+                         dtype: str = "bf16"):
+    """Gradients (dQ, dK, dV) of a packed variable-length batch, float64, in
+    the packed layouts ([total_q, Hq, d], [total_k, Hkv, d]); each sequence
+    goes through ``attention_bwd`` in the [1, H, N, d] layout."""
+    q, k, v, dout = (np.ascontiguousarray(t) for t in (q, k, v, dout))
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or len(cq) < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold n_seqs + 1 offsets")
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    to_b = lambda t, a, e: np.ascontiguousarray(t[a:e].transpose(1, 0, 2)[None])
+    for s in range(len(cq) - 1):
+        qa, qe, ka, ke = cq[s], cq[s + 1], ck[s], ck[s + 1]
+        if qe <= qa or ke <= ka:
+            continue                      # no query or no key: every gradient of the sequence is 0
+        gq, gk, gv = attention_bwd(to_b(q, qa, qe), to_b(k, ka, ke), to_b(v, ka, ke), to_b(dout, qa, qe),
+                                   causal=causal, scale=scale, dtype=dtype)
+        dq[qa:qe] = gq[0].transpose(1, 0, 2)
+        dk[ka:ke] = gk[0].transpose(1, 0, 2)
+        dv[ka:ke] = gv[0].transpose(1, 0, 2)
+    return dq, dk, dv
+

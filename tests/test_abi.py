@@ -243,3 +243,37 @@ def test_splitkv_invalid_arguments(lib, kw):
                                 dict(dtype=_lib.FA_DTYPE_F32)])
 def test_splitkv_unsupported(lib, kw):
     assert svalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
+
+
+# ---------------------------------------------------------------- fa_bwd_varlen
+BVGOOD = dict(q=4096, k=8192, v=12288, o=16384, lse=20480, do=24576, dq=28672, dk=32768, dv=36864, ws=40960,
+              cuq=45056, cuk=49152, n_seqs=3, max_q=700, max_k=800, total_q=1000, total_k=1200, Hq=8, Hkv=2,
+              d=128, causal=1, scale=0.125, dtype=_lib.FA_DTYPE_BF16)
+
+
+def bvvalidate(**kw):
+    a = dict(BVGOOD)
+    a.update(kw)
+    return _lib.fa_bwd_varlen_validate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                       a["ws"], a["cuq"], a["cuk"], a["n_seqs"], a["max_q"], a["max_k"],
+                                       a["total_q"], a["total_k"], a["Hq"], a["Hkv"], a["d"], a["causal"],
+                                       a["scale"], a["dtype"])
+
+
+def test_bwd_varlen_valid_arguments(lib):
+    assert bvvalidate() == _lib.FA_SUCCESS
+    assert bvvalidate(d=64, causal=0) == _lib.FA_SUCCESS
+    assert bvvalidate(n_seqs=0, cuq=None, cuk=None) == _lib.FA_SUCCESS
+
+
+@pytest.mark.parametrize("kw", [dict(n_seqs=-1), dict(max_k=-1), dict(total_q=-1), dict(Hkv=3), dict(cuk=None),
+                                dict(ws=None), dict(dq=None), dict(dk=None), dict(dv=28672 + 8),
+                                dict(lse=20480 + 2), dict(scale=math.inf), dict(dtype=5),
+                                dict(total_k=1 << 22, Hkv=8, d=128)])
+def test_bwd_varlen_invalid_arguments(lib, kw):
+    assert bvvalidate(**kw) == _lib.FA_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(dtype=_lib.FA_DTYPE_FP8_E4M3)])
+def test_bwd_varlen_unsupported(lib, kw):
+    assert bvvalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED

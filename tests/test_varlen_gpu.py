@@ -101,3 +101,64 @@ def test_varlen_mix_workload_sampled_rows():
         o_ref, lse_ref = oracle.attention(qs, ks, vs, causal=w["causal"], scale=scale, rows=rows)
         h, i = rows // L, rows % L
         compare_bf16(o[cu[s] + i, h], lse[h, cu[s] + i], o_ref, lse_ref, f"varlen_mix sequence {s} (len {L})")
+
+
+def run_varlen_bwd(x, do_bits, causal, scale):
+    from exact_attention_105_amd import bwd_varlen
+    q, k, v = (dev_bf16(x[t]) for t in ("q", "k", "v"))
+    do = dev_bf16(do_bits)
+    cq = torch.from_numpy(x["cu_q"]).to("cuda:0")
+    ck = torch.from_numpy(x["cu_k"]).to("cuda:0")
+    mq = int(np.diff(x["cu_q"]).max()) if len(x["cu_q"]) > 1 else 0
+    mk = int(np.diff(x["cu_k"]).max()) if len(x["cu_k"]) > 1 else 0
+    o, lse = fwd_varlen(q, k, v, cq, ck, mq, causal=causal, scale=scale)
+    outs = [torch.full(t.shape, float("nan"), dtype=torch.bfloat16, device=t.device) for t in (q, k, v)]
+    dq, dk, dv = bwd_varlen(q, k, v, o, lse, do, cq, ck, mq, mk, causal=causal, scale=scale,
+                            dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.synchronize()
+    return tuple(t.float().cpu().double().numpy() for t in (dq, dk, dv))
+
+
+# (query lengths, key lengths or None, Hq, Hkv, d, causal)
+BWD_CASES = [
+    ([128, 1, 300, 0, 129], None, 4, 2, 128, True),
+    ([77, 256, 5], [200, 100, 5], 2, 1, 64, True),
+    ([500, 3, 260], [1, 700, 0], 4, 2, 128, False),
+    ([300, 300], [300, 300], 8, 2, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[f"{c[0]}x{c[1]}H{c[2]}/{c[3]}d{c[4]}{'c' if c[5] else ''}"
+                                                 for c in BWD_CASES])
+def test_varlen_backward_matches_oracle(case):
+    from test_bwd_gpu import compare
+    from synth.inputs import f32_to_bf16_bits
+    lq, lk, Hq, Hkv, d, causal = case
+    lk = lq if lk is None else lk
+    x = make_varlen_inputs(np.array(lq), np.array(lk), Hq, Hkv, d, 5151 + sum(lq))
+    do_bits = f32_to_bf16_bits(np.random.default_rng(sum(lk)).standard_normal(x["q"].shape).astype(np.float32))
+    scale = 1.0 / math.sqrt(d)
+    say(f"varlen backward {case}")
+    got = run_varlen_bwd(x, do_bits, causal, scale)
+    ref = oracle.attention_bwd_varlen(x["q"], x["k"], x["v"], do_bits, x["cu_q"], x["cu_k"], causal=causal,
+                                      scale=scale)
+    compare(got, ref, f"varlen backward {case}")
+
+
+def test_varlen_backward_equal_lengths_match_the_batch_kernel_bit_for_bit():
+    from exact_attention_105_amd import bwd
+    from synth.inputs import f32_to_bf16_bits
+    n, N, Hq, Hkv, d = 2, 300, 4, 2, 128
+    x = make_varlen_inputs(np.full(n, N), np.full(n, N), Hq, Hkv, d, 78)
+    do_bits = f32_to_bf16_bits(np.random.default_rng(1).standard_normal(x["q"].shape).astype(np.float32))
+    got = run_varlen_bwd(x, do_bits, True, 0.09)
+    tb = lambda a, H: np.ascontiguousarray(a.reshape(n, N, H, d).transpose(0, 2, 1, 3))
+    qb, kb, vb, dob = (dev_bf16(tb(x["q"], Hq)), dev_bf16(tb(x["k"], Hkv)), dev_bf16(tb(x["v"], Hkv)),
+                       dev_bf16(tb(do_bits, Hq)))
+    o, lse = fwd(qb, kb, vb, causal=True, scale=0.09)
+    dq, dk, dv = bwd(qb, kb, vb, o, lse, dob, causal=True, scale=0.09)
+    torch.cuda.synchronize()
+    back = lambda t, H: t.float().cpu().double().numpy().transpose(0, 2, 1, 3).reshape(n * N, H, d)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, (back(dq, Hq), back(dk, Hkv), back(dv, Hkv))):
+        say(f"  equal lengths backward {name}: max |varlen - batch| {np.abs(g - r).max():.1e}")
+        assert np.array_equal(g, r), name

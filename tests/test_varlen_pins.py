@@ -69,3 +69,22 @@ def test_sequences_are_independent_and_follow_their_own_alignment():
     ck2 = np.concatenate([[0], np.cumsum([lk[s] for s in order])])
     o2, _ = oracle.attention_varlen(q2, k2, v2, cq2, ck2, causal=True, scale=0.5)
     assert np.array_equal(o2, np.concatenate([o[cq[s]:cq[s + 1]] for s in order]))
+
+
+def test_backward_reduces_to_the_batch_problem():
+    """The packed backward oracle: one sequence equals the batch backward of
+    the same tokens; sequences are independent (another sequence's tokens do
+    not change them); an empty side gives zero gradients."""
+    H, Hkv, d = 4, 2, 8
+    lq, lk = [6, 0, 9], [7, 3, 2]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q, k, v = packed(cq[-1], H, d, 11), packed(ck[-1], Hkv, d, 12), packed(ck[-1], Hkv, d, 13)
+    do = packed(cq[-1], H, d, 14)
+    dq, dk, dv = oracle.attention_bwd_varlen(q, k, v, do, cq, ck, causal=True, scale=0.5)
+    for s in (0, 2):
+        gq, gk, gv = oracle.attention_bwd(to_batch(q, cq, s), to_batch(k, ck, s), to_batch(v, ck, s),
+                                          to_batch(do, cq, s), causal=True, scale=0.5)
+        assert np.array_equal(dq[cq[s]:cq[s + 1]], gq[0].transpose(1, 0, 2))
+        assert np.array_equal(dk[ck[s]:ck[s + 1]], gk[0].transpose(1, 0, 2))
+        assert np.array_equal(dv[ck[s]:ck[s + 1]], gv[0].transpose(1, 0, 2))
+    assert not dk[ck[1]:ck[2]].any() and not dv[ck[1]:ck[2]].any()      # keys no query reads
