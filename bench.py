@@ -390,11 +390,35 @@ def varlen_bench(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    ms = timed(lambda: fwd_varlen(q, k, v, cq, ck, maxlen, causal=w["causal"], scale=scale, out=out, lse=lse),
-               args.steps, args.warmup)
     L = lens.astype(np.float64)
     pairs = np.sum(L * L / 2) if w["causal"] else np.sum(L * L)
     flops = 4.0 * w["Hq"] * w["d"] * pairs
+    if args.bwd:
+        from exact_attention_105_amd import bwd_varlen
+        from synth.inputs import make_grad_output
+        do = conv(make_grad_output(1, q.shape[0], w["Hq"], w["d"], w["seed"]).reshape(q.shape))
+        fwd_varlen(q, k, v, cq, ck, maxlen, causal=w["causal"], scale=scale, out=out, lse=lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(2 * w["Hq"] * q.shape[0], dtype=torch.float32, device=dev)
+        ms = timed(lambda: bwd_varlen(q, k, v, out, lse, do, cq, ck, maxlen, maxlen, causal=w["causal"], scale=scale,
+                                      dq=dq, dk=dk, dv=dv, workspace=ws), args.steps, args.warmup)
+        flops *= 2.5
+        tflops = flops / (ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS["bf16"]
+        print(json.dumps({
+            "metric": "varlen attention backward TFLOP/s (2.5x forward FLOPs) on 1 MI355X", "value": tflops,
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) inputs and dO)",
+            "config": {"workload": args.varlen + " backward", "n_seqs": int(len(lens)), "total_tokens": int(L.sum()),
+                       "max_seqlen": maxlen, "Hq": w["Hq"], "Hkv": w["Hkv"], "d": w["d"], "causal": w["causal"],
+                       "flops_per_step": flops},
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
+                         "traffic": None, "scope": "one fa_bwd_varlen call"},
+            "cpu_baseline": None}), flush=True)
+        return
+    ms = timed(lambda: fwd_varlen(q, k, v, cq, ck, maxlen, causal=w["causal"], scale=scale, out=out, lse=lse),
+               args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
     # the same sequences, zero-padded to the longest, through the fixed-length kernel
     B = len(lens)
@@ -534,11 +558,11 @@ def main():
     if args.rotate:
         rotate_bench(args)
         return
-    if args.bwd:
-        bwd_bench(args)
-        return
     if args.varlen:
         varlen_bench(args)
+        return
+    if args.bwd:
+        bwd_bench(args)
         return
 
     import torch
