@@ -405,6 +405,10 @@ def varlen_bench(args):
         flops *= 2.5
         tflops = flops / (ms * 1e-3) / 1e12
         peak = PEAK_TFLOPS["bf16"]
+        cpu = None
+        if args.cpu_budget > 0:
+            dob = make_grad_output(1, q.shape[0], w["Hq"], w["d"], w["seed"]).reshape(q.shape)
+            cpu = varlen_bwd_cpu_baseline(x, dob, lens, w, scale, args.cpu_budget)
         print(json.dumps({
             "metric": "varlen attention backward TFLOP/s (2.5x forward FLOPs) on 1 MI355X", "value": tflops,
             "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -414,8 +418,8 @@ def varlen_bench(args):
                        "max_seqlen": maxlen, "Hq": w["Hq"], "Hkv": w["Hkv"], "d": w["d"], "causal": w["causal"],
                        "flops_per_step": flops},
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
-                         "traffic": None, "scope": "one fa_bwd_varlen call"},
-            "cpu_baseline": None}), flush=True)
+                         "traffic": load_varlen_bwd_traffic(args.varlen), "scope": "one fa_bwd_varlen call"},
+            "cpu_baseline": cpu}), flush=True)
         return
     ms = timed(lambda: fwd_varlen(q, k, v, cq, ck, maxlen, causal=w["causal"], scale=scale, out=out, lse=lse),
                args.steps, args.warmup)
@@ -480,6 +484,43 @@ def varlen_cpu_baseline(x, lens, w, scale, budget_s: float):
         per *= 4
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{per} sampled (head, row) pairs of each of {len(lens)} sequences ({dt:.1f} s)"}
+
+
+def load_varlen_bwd_traffic(name: str):
+    """HBM bytes per fa_bwd_varlen call from the committed counter summary, if
+    taken on the current backward kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_bwd_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    return t.get("hbm_bytes_per_call") if t.get("kernel_source_hash") == bwd_source_hash() else None
+
+
+def varlen_bwd_cpu_baseline(x, dob, lens, w, scale, budget_s: float):
+    """The oracle's row-local dQ (6 * visible keys * d flops per row) on
+    sampled (head, row) pairs of every sequence, about budget_s seconds."""
+    import oracle
+    rng = np.random.default_rng(41)
+    cu = x["cu_q"]
+    per = 2
+    while True:
+        t0 = time.perf_counter()
+        flops = 0.0
+        for s in range(len(lens)):
+            L = int(lens[s])
+            seq = lambda a: np.ascontiguousarray(a[cu[s]:cu[s + 1]].transpose(1, 0, 2)[None])
+            rows = np.sort(rng.choice(w["Hq"] * L, size=min(per, w["Hq"] * L), replace=False))
+            oracle.bwd_dq_rows(seq(x["q"]), seq(x["k"]), seq(x["v"]), seq(dob), causal=w["causal"], scale=scale,
+                               rows=rows)
+            i = rows % L
+            flops += float(np.sum(6.0 * w["d"] * ((i + 1) if w["causal"] else L)))
+        dt = time.perf_counter() - t0
+        if dt >= 0.3 * budget_s or per >= 4096:
+            break
+        per *= 4
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"row-local dQ of {per} sampled (head, row) pairs of each of {len(lens)} sequences ({dt:.1f} s)"}
 
 
 def bwd_source_hash() -> str:
