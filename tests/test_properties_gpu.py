@@ -11,6 +11,9 @@ only sample rows.
   arithmetic per row either way, so the outputs must agree bit for bit.
 * A decode row (Nq = 1, bottom-right causal) equals the last row of the
   square causal problem on the same keys and values.
+* Causal problems whose keys and values exceed the 256 MiB memory-side cache
+  are scheduled in a different workgroup order; one launch per batch entry
+  (small enough for the default order) must give the same bits.
 """
 import math
 
@@ -109,6 +112,32 @@ def test_decode_is_last_causal_row(shape):
     dl = (l_full[:, :, -1:] - l_dec).abs()
     say(f"  max|dO|={d.max().item():.3e} max|dLSE|={dl.max().item():.3e}")
     assert d.max().item() <= BF16_MAX_ABS and dl.max().item() <= LSE_MAX_ABS
+
+
+CACHE_SIZED = [(32, 16, 16, 2048, 128), (16, 32, 8, 4300, 128), (64, 12, 12, 2048, 64)]
+
+
+@pytest.mark.parametrize("shape", CACHE_SIZED, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}N{s[3]}d{s[4]}" for s in CACHE_SIZED])
+def test_cache_sized_causal_order(shape):
+    from gpu_util import compare_bf16, oracle_ref, sample_rows
+    B, Hq, Hkv, N, d = shape
+    assert B * Hkv * N * d * 4 > (256 << 20) >= Hkv * N * d * 4     # whole launch grouped, one batch entry not
+    scale = 1.0 / math.sqrt(d)
+    say(f"cache-sized causal order: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d}")
+    x = make_inputs(B, Hq, Hkv, N, N, d, "bf16", 7000 + N + d)
+    q, k, v = bits_to_device(x["q"]), bits_to_device(x["k"]), bits_to_device(x["v"])
+    o = torch.full((B, Hq, N, d), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    fwd(q, k, v, causal=True, scale=scale, out=o, lse=lse)
+    for b in range(B):
+        ob, lb = fwd(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal=True, scale=scale)
+        assert torch.equal(o[b:b + 1], ob) and torch.equal(lse[b:b + 1], lb), f"batch entry {b} differs"
+    torch.cuda.synchronize()
+    rows = sample_rows(B, Hq, N, seed=N + d, per_head=16)
+    o_ref, lse_ref = oracle_ref(x, "bf16", True, scale, rows=rows)
+    of = o.float().cpu().double().numpy().reshape(-1, d)
+    lf = lse.cpu().double().numpy().reshape(-1)
+    compare_bf16(of[rows], lf[rows], o_ref, lse_ref, f"{rows.size} sampled rows")
 
 
 @pytest.mark.parametrize("name", ["gqa_causal", "gpt2"])
