@@ -124,6 +124,41 @@ __device__ __forceinline__ void copy_pair(const char* a, const char* b, int r0, 
     }
 }
 
+// Workgroup -> (key/value head kvflat = b*Hkv + hkv, member gi of its
+// `width` heads, tile rank t) over kvh*width units of n_tiles tiles.  The
+// hardware hands workgroups to the 8 XCDs round-robin (id mod 8).
+//  * group == 0: ranks outermost, units inner (all heads together, the
+//    heaviest causal tiles first).
+//  * group > 0 and kvh a multiple of 8: XCD x owns the key/value heads
+//    congruent to x mod 8 and takes them `group` at a time, ranks outermost
+//    within each group, so the workgroups resident on an XCD share the rows
+//    they stream through its L2 (stream_group picks this once those rows
+//    outgrow the memory-side cache).
+__device__ __forceinline__ void bwd_order(int bid, int kvh, int width, int n_tiles, int group,
+                                          int& kvflat, int& gi, int& t) {
+    if (group > 0 && (kvh & 7) == 0) {
+        const int xcd = bid & 7;
+        const int L = bid >> 3;
+        const int nkv = kvh >> 3;                        // key/value heads on this XCD
+        const int G = min(group, nkv);
+        const int per = G * width * n_tiles;             // workgroups of one full group
+        const int gidx = L / per;
+        const int r = L - gidx * per;
+        const int ge = min(G, nkv - gidx * G) * width;   // units in this group
+        t = r / ge;
+        const int hl = gidx * G * width + (r - t * ge);
+        const int kg = hl / width;
+        gi = hl - kg * width;
+        kvflat = xcd + 8 * kg;
+    } else {
+        const int n = kvh * width;
+        t = bid / n;
+        const int x = bid - t * n;
+        kvflat = x % kvh;
+        gi = x / kvh;
+    }
+}
+
 // Per-lane LDS offsets of a 32-row tile.
 template <int D>
 struct TileOffsets {
@@ -289,8 +324,8 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
     // workgroup -> (batch, key/value head, key tile); the key tiles with the
     // most visible queries (the first ones, for causal problems) come first
     const int kvh = p.B * p.Hkv;
-    const int kt = blockIdx.x / kvh;
-    const int kvflat = blockIdx.x - kt * kvh;
+    int kt, kvflat, unused;
+    bwd_order(blockIdx.x, kvh, 1, p.n_ktiles, p.group_dkv, kvflat, unused, kt);
     const int b = kvflat / p.Hkv;
     const int hkv = kvflat - b * p.Hkv;
     const int k0 = kt * C::ROWS;
@@ -461,12 +496,9 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams pin) {
 
     // workgroup -> (batch, query head, query tile): heads first, and for
     // causal problems the query tiles with the most keys first
-    const int n_heads = p.B * p.Hq;
-    const int t_ord = blockIdx.x / n_heads;
-    const int x = blockIdx.x - t_ord * n_heads;
     const int kvh = p.B * p.Hkv;
-    const int kvflat = x % kvh;
-    const int gi = x / kvh;
+    int t_ord, kvflat, gi;
+    bwd_order(blockIdx.x, kvh, p.group, p.n_qtiles, p.group_dq, kvflat, gi, t_ord);
     const int b = kvflat / p.Hkv;
     const int hkv = kvflat - b * p.Hkv;
     const int hq = hkv * p.group + gi;
@@ -573,6 +605,11 @@ template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     using C = BwdCfg<D>;
     BwdParams pp = p;
+    // dK/dV workgroups stream Q and dO rows, dQ workgroups K and V rows
+    const long long q_rows = VARLEN ? (long long)p.total_q : (long long)p.B * p.Nq;
+    const long long k_rows = VARLEN ? (long long)p.total_k : (long long)p.B * p.Nk;
+    pp.group_dkv = stream_group(q_rows * p.Hq * D * 2 * 2);
+    pp.group_dq = stream_group(k_rows * p.Hkv * D * 2 * 2);
     const int64_t R = VARLEN ? (int64_t)p.total_q * p.Hq : (int64_t)p.B * p.Hq * p.Nq;
     void* args[] = {&pp};
     hipError_t e = hipSuccess;

@@ -22,6 +22,8 @@ struct BwdParams {
     int causal_shift;    // Nk - Nq: key j visible to query i iff j <= i + causal_shift
     int n_qtiles;        // dQ kernel: query tiles per head
     int n_ktiles;        // dK/dV kernel: key tiles per key/value head
+    int group_dkv;       // workgroup orders (bwd_order): 0 heads first, G > 0 each XCD's
+    int group_dq;        // key/value heads G at a time
     float c;             // scale * log2(e), signed
     float scale;         // multiplies dQ and dK
     // Variable-length batches (packed [tokens, H, d] layouts): B counts

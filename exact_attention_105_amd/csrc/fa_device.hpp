@@ -43,7 +43,7 @@ struct FwdParams {
     float o_scale;      // multiplies the normalised output (sv for fp8, 1 for bf16)
     uint32_t q_sign;    // XOR mask applied to Q bit patterns (flips the sign when scale < 0)
     int kv_group;       // causal order: 0 walks all heads together; G > 0 takes each XCD's
-                        // key/value heads G at a time (causal_kv_group)
+                        // key/value heads G at a time (stream_group)
 };
 
 __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -183,9 +183,11 @@ __device__ __forceinline__ void tile_of(const FwdParams& p, int bid, int& b, int
     qt = CAUSAL ? (p.n_qtiles - 1 - t_ord) : t_ord;
 }
 
-// kv_group for a causal prefill launch whose key and value tensors hold
-// kv_bytes bytes in all: 2 above the 256 MiB memory-side cache, else 0.
-inline int causal_kv_group(long long kv_bytes) { return kv_bytes > (256LL << 20) ? 2 : 0; }
+// Group size for the XCD-local orders of launches whose workgroups all
+// stream one set of per-head tensors (keys and values for the forward and
+// dQ kernels, queries and output gradients for dK/dV) holding `bytes` bytes
+// in all: 2 above the 256 MiB memory-side cache, else 0 (heads first).
+inline int stream_group(long long bytes) { return bytes > (256LL << 20) ? 2 : 0; }
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;

@@ -448,7 +448,7 @@ static hipError_t launch_one(const FwdParams& p, const VarlenParams& vp, hipStre
     VarlenParams vv = vp;
     pp.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
     const long long kv_rows = VARLEN ? (long long)vp.total_k : (long long)p.B * p.Nk;
-    pp.kv_group = causal_kv_group(kv_rows * p.Hkv * D * 2 * 2);
+    pp.kv_group = stream_group(kv_rows * p.Hkv * D * 2 * 2);
     const long long grid = (long long)pp.n_qtiles * pp.n_heads;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;

@@ -312,7 +312,7 @@ template <bool CAUSAL>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     FwdParams pp = p;
     pp.n_qtiles = (p.Nq + Fp8Cfg::BM - 1) / Fp8Cfg::BM;
-    pp.kv_group = causal_kv_group((long long)p.B * p.Nk * p.Hkv * 128 * 2);
+    pp.kv_group = stream_group((long long)p.B * p.Nk * p.Hkv * 128 * 2);
     const long long grid = (long long)pp.n_qtiles * pp.n_heads;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;

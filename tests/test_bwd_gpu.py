@@ -150,3 +150,37 @@ def test_backward_full_size_long_context():
     say(f"  |sum_j dK_j| / ||dK col||: {rel_k:.3e}; |sum_j dV_j - sum_i dO_i| / max: {rel_v:.3e}")
     assert rel_k <= 2e-2, rel_k
     assert rel_v <= 1e-2, rel_v
+
+
+BIG = [(32, 16, 16, 2048, 128, True), (16, 32, 8, 4300, 128, False), (64, 12, 12, 2048, 64, True)]
+
+
+@pytest.mark.parametrize("shape", BIG, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}N{s[3]}d{s[4]}{'c' if s[5] else 'n'}" for s in BIG])
+def test_backward_cache_sized_order(shape):
+    """Problems whose streamed rows (Q and dO for dK/dV, K and V for dQ)
+    exceed the 256 MiB memory-side cache run in a different workgroup order;
+    one call per batch entry (small enough for the default order) must give
+    the same bits, and sampled dQ rows must match the oracle."""
+    B, Hq, Hkv, N, d, causal = shape
+    assert B * Hq * N * d * 4 > (256 << 20) >= Hq * N * d * 4
+    scale = 1.0 / math.sqrt(d)
+    x = make_inputs(B, Hq, Hkv, N, N, d, "bf16", 9100 + N + d)
+    do_bits = make_grad_output(B, Hq, N, d, 9100 + N + d)
+    say(f"backward cache-sized order: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}")
+    q, k, v = (dev_bf16(x[n]) for n in ("q", "k", "v"))
+    do = dev_bf16(do_bits)
+    o, lse = fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    for b in range(B):
+        s = slice(b, b + 1)
+        g1 = bwd(q[s], k[s], v[s], o[s], lse[s], do[s], causal=causal, scale=scale)
+        for name, full, one in zip(("dQ", "dK", "dV"), (dq, dk, dv), g1):
+            assert torch.equal(full[s], one), f"{name} of batch entry {b} differs"
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(N + d).choice(B * Hq * N, size=256, replace=False)
+    ref = oracle.bwd_dq_rows(x["q"], x["k"], x["v"], do_bits, causal=causal, scale=scale, rows=rows)
+    got = dq.float().cpu().double().numpy().reshape(-1, d)[rows]
+    rr = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    mx = float(np.abs(got - ref).max() / np.abs(ref).max())
+    say(f"  sampled dQ rows: rRMSE={rr:.3e} max/|G|max={mx:.3e}")
+    assert rr <= G_RRMSE and mx <= G_MAX_REL
