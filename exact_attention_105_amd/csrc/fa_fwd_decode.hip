@@ -291,22 +291,41 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int 
 
 // Combine the n_splits partials of one output row (one workgroup per row,
 // one thread per column of d): weights 2^(lse_s - M), M the largest lse_s.
+// The split LSEs are read in parallel (thread s reads splits s and s + kD),
+// the maximum and the sum of the weights are reduced across the two waves,
+// the weights go to LDS, and each thread then sums its column over the
+// splits with several loads in flight.
 __global__ __launch_bounds__(kD) void fa_decode_merge_kernel(FwdParams p, int n_splits, const float* ws) {
+    __shared__ float wgt[2 * kD];
+    __shared__ float red[2][kD / 64];
     const int64_t R = (int64_t)p.B * p.Hq * p.Nq;
     const int64_t r = blockIdx.x;
     const int t = threadIdx.x;
+    const int wv = t >> 6;
     const float* lse2 = ws + (int64_t)n_splits * R * kD;
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, lse2[(int64_t)s * R + r]);
-    float L = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < n_splits; ++s) {
-            const float ls = lse2[(int64_t)s * R + r];
-            const float a = ls == -INFINITY ? 0.f : fast_exp2(ls - M);
-            L += a;
-            acc += a * ws[((int64_t)s * R + r) * kD + t];
-        }
-    }
+    const float l0 = t < n_splits ? lse2[(int64_t)t * R + r] : -INFINITY;
+    const float l1 = t + kD < n_splits ? lse2[(int64_t)(t + kD) * R + r] : -INFINITY;
+    float m = fmaxf(l0, l1);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((t & 63) == 0) red[0][wv] = m;
+    __syncthreads();
+    const float M = fmaxf(red[0][0], red[0][1]);
+    const float a0 = (M == -INFINITY || l0 == -INFINITY) ? 0.f : fast_exp2(l0 - M);
+    const float a1 = (M == -INFINITY || l1 == -INFINITY) ? 0.f : fast_exp2(l1 - M);
+    wgt[t] = a0;
+    wgt[t + kD] = a1;
+    float sum = a0 + a1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    if ((t & 63) == 0) red[1][wv] = sum;
+    __syncthreads();
+    const float L = red[1][0] + red[1][1];
+    const float* col = ws + r * kD + t;
+    const int64_t stride = R * kD;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int sp = 0; sp < n_splits; ++sp) acc += wgt[sp] * col[sp * stride];
     const float o = L > 0.f ? acc / L : 0.f;
     reinterpret_cast<__bf16*>(p.o)[r * kD + t] = static_cast<__bf16>(o);
     if (t == 0 && p.lse != nullptr) p.lse[r] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
