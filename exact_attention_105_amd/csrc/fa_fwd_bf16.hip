@@ -41,12 +41,14 @@
 //
 // Online softmax with a lazily updated reference: the exponent reference of
 // a row only moves when its running maximum exceeds the reference by more
-// than kRescaleLog2 (in log2 units); until then the exponentials are at most
-// 2^kRescaleLog2 and no rescale of O and l is needed.  The result is the
-// same softmax (the reference cancels between numerator and denominator)
-// with far fewer rescales (the idea of page "FlashAttention 4", centron.de,
-// section on smarter online-softmax rescaling; the threshold is this
-// library's choice).  A wave skips the O rescale when none of its rows moved.
+// than kRescaleLog2 (in log2 units), and the wave only looks at the row
+// maxima when some lane's sum of exponentials against the current reference
+// passes kSumLimit; until then no rescale of O and l is needed and no row
+// maximum is formed.  The result is the same softmax (the reference cancels
+// between numerator and denominator) with far fewer rescales (the idea of
+// page "FlashAttention 4", centron.de, section on smarter online-softmax
+// rescaling; the thresholds are this library's choice).  A wave skips the O
+// rescale when none of its rows moved.
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -56,6 +58,9 @@
 namespace fa {
 
 constexpr float kRescaleLog2 = 8.0f;
+// A lane whose 16 exponentials sum past this sends its wave to the reference
+// move; a sum above it implies some exponential above 2^kRescaleLog2.
+constexpr float kSumLimit = 4096.0f;      // 2^(kRescaleLog2 + 4)
 // Reference of a row that has seen no visible key: finite, so the first move
 // gives alpha = exp2(kNoRef - m) = 0 and an unmoved row exp2(0) = 1 without
 // special cases; any visible score moves it.
@@ -265,14 +270,12 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
 
     f32x16 o[C::NQB][C::DB];
     float mref[C::NQB];      // exponent reference per row, log2 units
-    float thr[C::NQB];       // raw score above which the reference must move
     float l[C::NQB];         // this lane's part of the row sums
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) o[qb][db] = f32x16{};
         mref[qb] = kNoRef;
-        thr[qb] = -INFINITY;     // the first visible score sets the reference
         l[qb] = 0.f;
     }
 
@@ -294,6 +297,25 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         const lds_char* kb = smem + STG * C::STAGE;
         const lds_char* vb = kb + C::TILE;
         const bool need_mask = (key0 + C::BN > p.Nk) || (CAUSAL && key0 + C::BN - 1 > wq0 + p.causal_shift);
+
+        // S^T of one 32-key half for one 32-row query block, from the K tile
+        // in LDS (also used to recompute scores in the rare reference move).
+        auto scores = [&](int kh, int qb) {
+            f32x16 acc{};
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks)
+                acc = mfma_bf16_32x32x16(lds_b128(kb + k_off[ks] + kh * 32 * C::ROW), qf[qb][ks], acc);
+            return acc;
+        };
+        // Mask keys past Nk and, for causal problems, keys after each query's
+        // diagonal.  Only tiles that straddle either edge pay.
+        auto mask = [&](int kh, int qb, f32x16& sv) {
+            const int qrow = wq0 + 32 * qb + n;
+            const int lim = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - key0 - 32 * kh - 4 * g;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (8 * (i >> 2) + (i & 3) > lim) sv[i] = -INFINITY;
+        };
 
         // S^T of every 32-key half of the tile first (64-key tiles: the MFMA
         // pipe works through the second half while the first half's softmax
@@ -325,42 +347,50 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
         // recurrence.
 #pragma unroll
         for (int kh = 0; kh < C::KH; ++kh) {
-            // Mask keys past Nk and, for causal problems, keys after each
-            // query's diagonal.  Only tiles that straddle either edge pay.
             if (need_mask) {
 #pragma unroll
-                for (int qb = 0; qb < C::NQB; ++qb) {
-                    const int qrow = wq0 + 32 * qb + n;
-                    const int lim = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - key0 - 32 * kh - 4 * g;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (8 * (i >> 2) + (i & 3) > lim) s[kh][qb][i] = -INFINITY;
-                }
+                for (int qb = 0; qb < C::NQB; ++qb) mask(kh, qb, s[kh][qb]);
             }
 
             bf16x8 pb[C::NQB][2];
 #pragma unroll
             for (int qb = 0; qb < C::NQB; ++qb) {
                 f32x16& sv = s[kh][qb];
-                // Each lane compares the maximum of its own 16 raw scores with
-                // the threshold; only when some lane passes it does the wave
-                // form the row maxima and move references (rare after the
-                // first tile).
-                const float lm = max16(sv);
-                if (__builtin_amdgcn_ballot_w64(lm > thr[qb]) != 0) {
-                    const float mx = pair_max(lm) * p.c;            // row max of the tile, log2 units
+                // Exponentials against the current reference first.  Only when
+                // some lane's sum of its 16 exceeds kSumLimit does the wave
+                // recompute these scores, form the row maxima and move
+                // references -- rare after the first tile, which has no
+                // reference yet and takes that path directly.  Every accepted
+                // exponential is therefore at most kSumLimit, and a row whose
+                // sum passed it has a score above its reference by more than
+                // kRescaleLog2, so it moves and its new exponentials are at
+                // most 1.
+                bool slow = j == 0;
+                float ls = 0.f;
+                if (!slow) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(fmaf(sv[i], p.c, -mref[qb]));
+                    ls = sum16(sv);
+                    if (__builtin_amdgcn_ballot_w64(!(ls <= kSumLimit)) != 0) {
+                        sv = scores(kh, qb);
+                        if (need_mask) mask(kh, qb, sv);
+                        slow = true;
+                    }
+                }
+                if (slow) {
+                    const float mx = pair_max(max16(sv)) * p.c;     // row max of the half, log2 units
                     const bool move = mx > mref[qb] + kRescaleLog2;
                     const float mnew = move ? mx : mref[qb];
                     const float alpha = fast_exp2(mref[qb] - mnew);  // 0 at the first move, 1 if unmoved
                     mref[qb] = mnew;
-                    thr[qb] = (mnew + kRescaleLog2) / p.c;
                     l[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < C::DB; ++db) o[qb][db] *= alpha;
-                }
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(fmaf(sv[i], p.c, -mref[qb]));
-                l[qb] += sum16(sv);
+                    for (int i = 0; i < 16; ++i) sv[i] = fast_exp2(fmaf(sv[i], p.c, -mref[qb]));
+                    ls = sum16(sv);
+                }
+                l[qb] += ls;
 #pragma unroll
                 for (int h8 = 0; h8 < 2; ++h8) {
                     u32x4 pk;
