@@ -131,6 +131,46 @@ def test_lse_optional():
     assert l2 is None and torch.equal(o1, o2)
 
 
+# Keys whose norms grow along the sequence: each row's running maximum keeps
+# rising, so the kernels' lazily moved exponent reference has to move many
+# times after the first key tile (N(0,1) inputs almost never need that).
+GROWING = [
+    (1, 2, 2, 700, 700, 128, False),
+    (1, 2, 2, 700, 700, 128, True),
+    (2, 2, 1, 513, 600, 64, False),
+    (1, 3, 3, 600, 600, 64, True),
+]
+
+
+def _growing_keys(x, growth):
+    from synth.inputs import f32_to_bf16_bits
+    k = (x["k"].astype(np.uint32) << 16).view(np.float32)
+    nk = k.shape[2]
+    ramp = (1.0 + growth * np.arange(nk, dtype=np.float32) / nk)[None, None, :, None]
+    x = dict(x)
+    x["k"] = f32_to_bf16_bits(k * ramp).reshape(k.shape)
+    return x
+
+
+@pytest.mark.parametrize("shape", GROWING, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}Nq{s[3]}Nk{s[4]}d{s[5]}{'c' if s[6] else 'n'}"
+                                                 for s in GROWING])
+def test_reference_moves_mid_row(shape):
+    B, Hq, Hkv, Nq, Nk, d, causal = shape
+    say(f"case {shape}")
+    x = _growing_keys(make_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", 2000 + sum(shape)), growth=9.0)
+    scale = 1.0 / math.sqrt(d)
+    # the inputs do what they are for: in the last query row, the maximum
+    # score (log2 units) of the last 32 keys exceeds that of the first 32 by
+    # more than 12, so its reference moves after the first tile
+    q = (x["q"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    k = (x["k"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    s2 = q[0, 0, -1] @ k[0, 0].T * scale / math.log(2)
+    assert s2[-32:].max() - s2[:32].max() > 12, (s2[:32].max(), s2[-32:].max())
+    o, lse = run_gpu(x, "bf16", causal, scale)
+    o_ref, lse_ref = oracle_ref(x, "bf16", causal, scale)
+    compare_bf16(o, lse, o_ref, lse_ref, str(shape))
+
+
 # ------------------------------------------------------------------ full-size workloads
 BF16_CONFIGS = ["tiny", "gpt2", "gpt2_causal", "long16k_causal", "gqa_causal", "gqa_decode"]
 
