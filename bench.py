@@ -89,17 +89,27 @@ def load_traffic(cfg, variant: str = ""):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (first /proc/cpuinfo entry) and logical CPUs."""
+    """The host CPU's model name, sockets and physical cores (from
+    /proc/cpuinfo) and the logical CPUs this process may use."""
     name = "unknown"
+    sockets, cores = set(), set()
     try:
         with open("/proc/cpuinfo") as f:
+            phys = "0"
             for line in f:
-                if line.startswith("model name"):
-                    name = line.split(":", 1)[1].strip()
-                    break
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and name == "unknown":
+                    name = val
+                elif key == "physical id":
+                    phys = val
+                    sockets.add(val)
+                elif key == "core id":
+                    cores.add((phys, val))
     except OSError:
         pass
-    return f"{name}, {len(os.sched_getaffinity(0))} logical CPUs available"
+    topo = f", {len(sockets)} socket(s), {len(cores)} physical cores" if sockets and cores else ""
+    return f"{name}{topo}, {len(os.sched_getaffinity(0))} logical CPUs available"
 
 
 def cpu_baseline(cfg, x, budget_s: float):
@@ -699,7 +709,11 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Nq": cfg.Nq,
                    "Nk": cfg.Nk, "d": cfg.d, "causal": cfg.causal, "flops_per_step": cfg.flops,
                    "algorithmic_bytes_per_step": cfg.algorithmic_bytes,
-                   "kernel_source_hash": kernel_source_hash(cfg), "n_splits": n_splits},
+                   "kernel_source_hash": kernel_source_hash(cfg), "n_splits": n_splits,
+                   # the fused kernel keeps no score matrix: against the fp32 S
+                   # that naive attention would write to and read back from HBM
+                   "workspace_bytes": 0 if not n_splits else n_splits * cfg.B * cfg.Hq * cfg.Nq * (cfg.d + 1) * 4,
+                   "naive_scores_fp32_bytes": cfg.B * cfg.Hq * cfg.Nq * cfg.Nk * 4},
         "roofline": roof,
         "wall_s_timed": wall,
     }
