@@ -87,9 +87,9 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * fa_fwd_validate -- the argument checks fa_fwd performs before launching,
- * as a pure host function (it makes no HIP call and touches no memory
- * behind the pointers).  Returns the status fa_fwd would return for these
- * arguments short of a launch failure.
+ * as a pure host function (it makes no HIP call and touches no device
+ * memory; for FP8 it reads the three host-side descale values).  Returns the
+ * status fa_fwd would return for these arguments short of a launch failure.
  */
 fa_status_t fa_fwd_validate(const void* q, const void* k, const void* v, const void* o,
                             const float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
