@@ -220,6 +220,25 @@ __device__ __forceinline__ bf16x8 lds_b128(const lds_char* p) {
 // vmcnt(n) with the other counters left alone (gfx9 encoding)
 #define FA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
 
+// Instruction order inside one MFMA phase (a scheduling region between two
+// sched_barriers): the LDS operand reads of the first PF MFMAs (RPM reads per
+// MFMA) first, then each MFMA followed by the reads of the MFMA PF places
+// later, then the last PF MFMAs -- so that each MFMA finds its operand read
+// PF MFMAs earlier instead of waiting on the read just before it.
+template <int NMFMA, int RPM, int PF>
+__device__ __forceinline__ void order_reads_ahead() {
+    if constexpr (PF > 0) {
+        constexpr int P = PF < NMFMA ? PF : NMFMA;
+        __builtin_amdgcn_sched_group_barrier(0x100, P * RPM, 0);
+#pragma unroll
+        for (int i = 0; i < NMFMA - P; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
+    }
+}
+
 // 8 bytes per lane through the 8-bit transposing LDS read: within each group
 // of 16 lanes, lane i receives byte i%8 of the 8 bytes read by lanes
 // i/8 + 2r, r = 0..7 (in that order).

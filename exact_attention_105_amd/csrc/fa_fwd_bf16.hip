@@ -75,6 +75,14 @@ constexpr float kNoRef = -1.0e30f;
 #ifndef FA_BF16_OCC
 #define FA_BF16_OCC 3
 #endif
+// LDS operand reads kept in flight ahead of the MFMAs of the S^T and O^T
+// phases at d = 128 (0: the compiler's order, which keeps one in flight).
+#ifndef FA_BF16_PF_S
+#define FA_BF16_PF_S 3
+#endif
+#ifndef FA_BF16_PF_V
+#define FA_BF16_PF_V 3
+#endif
 #ifndef FA_BF16_RW128
 #define FA_BF16_RW128 32     // query rows per wave at d = 128 (32 or 64)
 #endif
@@ -118,6 +126,8 @@ struct Bf16Cfg {
     static constexpr int CPW = CHUNKS / NW;      // ... per wave
     static constexpr int RPC = 1024 / ROW;       // rows per 1 KiB chunk
     static constexpr int KS = D / 16;            // MFMA steps over d for S
+    static constexpr int PF_S = D == 128 ? FA_BF16_PF_S : 0;   // K reads ahead of the S^T MFMAs
+    static constexpr int PF_V = D == 128 ? FA_BF16_PF_V : 0;   // V^T read pairs ahead of the O^T MFMAs
     static constexpr int DB = D / 32;            // 32-wide blocks of d in O
     // LDS swizzles, in 16-byte units (LDS: 64 banks of 4 bytes, 256 B per cycle).
     // K: the 16 rows one ds_read_b128 cycle touches must cover all 16 units:
@@ -336,6 +346,7 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                 for (int qb = 0; qb < C::NQB; ++qb) s[kh][qb] = mfma_bf16_32x32x16(a, qf[qb][ks], s[kh][qb]);
             }
         }
+        if constexpr (C::KH == 1 && C::NQB == 1) order_reads_ahead<C::KS, 1, C::PF_S>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         // The next tile's copies go out after the score MFMAs, in the wait
@@ -414,6 +425,7 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                     for (int qb = 0; qb < C::NQB; ++qb) o[qb][db] = mfma_bf16_32x32x16(a, pb[qb][h8], o[qb][db]);
                 }
             }
+            if constexpr (C::NQB == 1) order_reads_ahead<2 * C::DB, 2, C::PF_V>();
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(0);
         }

@@ -31,6 +31,13 @@
 
 namespace fa {
 
+#ifndef FA_FP8_PF_S
+#define FA_FP8_PF_S 3        // K read pairs kept ahead of the S^T MFMAs (0: the compiler's order)
+#endif
+#ifndef FA_FP8_PF_V
+#define FA_FP8_PF_V 2        // V^T read quads kept ahead of the O^T MFMAs
+#endif
+
 constexpr float kP8Offset = 6.0f;   // log2 of the factor carried by the exponentials
 constexpr float kP8Slack = 2.0f;    // log2 growth of the max tolerated before rescaling
 // Reference of a row that has seen no visible key: finite, so the first move
@@ -210,6 +217,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
                 s[kh] = mfma_fp8_32x32x64(a, qf[ks], s[kh]);
             }
         }
+        order_reads_ahead<4, 2, FA_FP8_PF_S>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         // the next tile's copies go out in the wait before the scores can be read
@@ -267,6 +275,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
             }
             o[db] = mfma_fp8_32x32x64(a, pb, o[db]);
         }
+        order_reads_ahead<C::DB, 4, FA_FP8_PF_V>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
     }
