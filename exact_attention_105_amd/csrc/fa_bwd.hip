@@ -73,6 +73,15 @@ struct BwdCfg {
 // non-causal kernel (which keeps more loop state) would spill with two.
 enum KvMode { kBoth = 0, kOnlyDV = 1, kOnlyDK = 2 };
 
+// LDS operand reads kept in flight ahead of the MFMAs of the score phases
+// (S, dP) and of the accumulation phases (dV, dK, dQ); 0: the compiler's order.
+#ifndef FA_BWD_PF_S
+#define FA_BWD_PF_S 4
+#endif
+#ifndef FA_BWD_PF_V
+#define FA_BWD_PF_V 3
+#endif
+
 #ifndef FA_BWD_SPLIT_DKV
 #define FA_BWD_SPLIT_DKV 1   // d = 128: dV and dK in two kernels (fewer registers each)
 #endif
@@ -416,6 +425,7 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
                     dp[hh] = mfma_bf16_32x32x16(lds_b128(ob + 32 * hh * C::ROW + off.b[ks]), vf[ks], dp[hh]);
             }
         }
+        order_reads_ahead<NH * C::KS * (DO_DK ? 2 : 1), 1, FA_BWD_PF_S>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (it + 1 < n_it) issue(it + 1, STG ^ 1);
@@ -462,6 +472,7 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
                     if constexpr (DO_DV) dv[db] = mfma_bf16_32x32x16(tr_operand<D>(obh, off, db, st), pp[st], dv[db]);
                     if constexpr (DO_DK) dk[db] = mfma_bf16_32x32x16(tr_operand<D>(qbh, off, db, st), pd[st], dk[db]);
                 }
+            order_reads_ahead<2 * C::DB * ((DO_DV ? 1 : 0) + (DO_DK ? 1 : 0)), 2, FA_BWD_PF_V>();
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(0);
         }
@@ -567,6 +578,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams pin) {
             s = mfma_bf16_32x32x16(lds_b128(kb + off.b[ks]), qf[ks], s);
             dp = mfma_bf16_32x32x16(lds_b128(vb + off.b[ks]), df[ks], dp);
         }
+        order_reads_ahead<2 * C::KS, 1, FA_BWD_PF_S>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (j + 1 < n_tiles) issue(j + 1, STG ^ 1);
@@ -588,6 +600,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams pin) {
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) acc[db] = mfma_bf16_32x32x16(tr_operand<D>(kb, off, db, st), pd[st], acc[db]);
+        order_reads_ahead<2 * C::DB, 2, FA_BWD_PF_V>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
     };
