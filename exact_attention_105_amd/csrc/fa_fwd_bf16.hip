@@ -29,6 +29,11 @@
 // and V^T fragment read from LDS to two MFMAs, but needs the accumulators in
 // AGPRs and runs one workgroup per CU; measured slower.
 //
+// Within each MFMA phase the LDS operand reads are ordered to run PF_S (K)
+// or PF_V (V^T pairs) MFMAs ahead of their products (order_reads_ahead in
+// fa_device.hpp): left to itself the scheduler keeps one read in flight, and
+// every MFMA waits on the read just before it.
+//
 // K/V staging: the global loads go straight into LDS (global_load_lds_dwordx4,
 // 1 KiB per wave instruction, no staging registers), NSTAGE tiles deep, with
 // one barrier per tile.  LDS
