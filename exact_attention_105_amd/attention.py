@@ -15,6 +15,19 @@ from . import _lib
 _FP8_TYPES = (torch.uint8, torch.float8_e4m3fn)
 
 
+def _on_device(dev, **tensors):
+    """Every given tensor (None is skipped) is a contiguous GPU tensor on
+    ``dev``: the library writes through raw pointers, so a tensor elsewhere,
+    or a strided view, must be refused before the call."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != dev:
+            raise ValueError(f"{name} must be a GPU tensor on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
         scale: float | None = None, descale=None, out: torch.Tensor | None = None,
         lse: torch.Tensor | None = None, return_lse: bool = True):
@@ -61,6 +74,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq)
                             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    _on_device(q.device, out=out, lse=lse)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = _lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                      lse.data_ptr() if lse is not None else None,
@@ -99,13 +113,18 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
         n_splits = default_splits(B, Hq, Hkv, Nq, Nk)
     if out is None:
         out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, Hq, Nq, d):
+        raise ValueError("out must be a contiguous bfloat16 [B, Hq, Nq, d] tensor")
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
     need = n_splits * B * Hq * Nq * (d + 1)
     if workspace is None and n_splits > 1:
         workspace = torch.empty(max(need, 1), dtype=torch.float32, device=q.device)
     elif workspace is not None and (workspace.dtype != torch.float32 or workspace.numel() < need):
         raise ValueError(f"workspace must hold {need} float32 values")
+    _on_device(q.device, k=k, v=v, out=out, lse=lse, workspace=workspace)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = _lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                              B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale, _lib.FA_DTYPE_BF16, n_splits,
@@ -149,6 +168,7 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    _on_device(q.device, k=k, v=v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, out=out, lse=lse)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = _lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), n_seqs, int(max_seqlen_q),
@@ -195,6 +215,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
         workspace = torch.empty(max(2 * B * Hq * Nq, 1), dtype=torch.float32, device=q.device)
     elif workspace.dtype != torch.float32 or workspace.numel() < 2 * B * Hq * Nq:
         raise ValueError("workspace must hold 2*B*Hq*Nq float32 values")
+    _on_device(q.device, k=k, v=v, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv, workspace=workspace)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = _lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
@@ -247,6 +268,8 @@ def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
         workspace = torch.empty(max(2 * Hq * total_q, 1), dtype=torch.float32, device=q.device)
     elif workspace.dtype != torch.float32 or workspace.numel() < 2 * Hq * total_q:
         raise ValueError("workspace must hold 2*Hq*total_q float32 values")
+    _on_device(q.device, k=k, v=v, o=o, lse=lse, dout=dout, dq=dq, dk=dk, dv=dv, workspace=workspace,
+               cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = _lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
@@ -298,8 +321,13 @@ def rotate_quantize(x: torch.Tensor, *, rotate: bool = True, signs=None,
         raise ValueError("codes must be a contiguous float8_e4m3fn/uint8 tensor shaped like x")
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    elif scale.dtype != torch.float32 or scale.numel() < 1:
+        raise ValueError("scale must be a float32 tensor of at least one element")
     if work is None:
         work = torch.empty(1, dtype=torch.float32, device=x.device)
+    elif work.dtype != torch.float32 or work.numel() < 1:
+        raise ValueError("work must be a float32 tensor of at least one element")
+    _on_device(x.device, codes=codes, scale=scale, work=work)
     if signs is not None and len(signs) != d:
         raise ValueError("signs must have one entry per feature")
     bits = sign_bits(signs) if signs is not None else None
