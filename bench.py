@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}   # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s on 1 MI355X (bf16/fp8) and % of MFMA peak"
+SHORT_WORKLOADS = ("tiny", "gpt2", "gpt2_causal", "gqa_decode")
 
 
 def kernel_source(cfg) -> str:
@@ -575,7 +576,9 @@ def bwd_cpu_baseline(cfg, x, dob, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for the short workloads tiny, gpt2, gpt2_causal "
+                         "and gqa_decode, whose launches last tens to hundreds of microseconds)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="long16k_causal")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -596,6 +599,9 @@ def main():
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
     args = ap.parse_args()
+    if args.steps is None:
+        short = not (args.varlen or args.bwd or args.rotate or args.gemm_reference or args.copy_bytes)
+        args.steps = 200 if short and args.config in SHORT_WORKLOADS else 20
     if args.copy_bytes > 0:
         copy_calibration(args)
         return
