@@ -38,6 +38,7 @@ extern "C" fa_status_t fa_fwd_validate(const void* q, const void* k, const void*
     if (q_elems > kMaxElems || kv_elems > kMaxElems) return FA_ERROR_INVALID_VALUE;
     const int64_t rows = (int64_t)B * Hq * Nq;
     if (rows > 0) {
+        if (Nk == 0) return FA_ERROR_INVALID_VALUE;   // rows to compute but no key to attend to
         if (q == nullptr || o == nullptr) return FA_ERROR_INVALID_VALUE;
         if (!aligned(q, 16) || !aligned(o, 16)) return FA_ERROR_INVALID_VALUE;
         if (lse != nullptr && !aligned(lse, 4)) return FA_ERROR_INVALID_VALUE;

@@ -65,7 +65,8 @@ typedef enum {
  *                         the caller does not need it.
  * Sizes: B >= 0, Hq >= 1, Hkv >= 1 with Hq % Hkv == 0, Nq >= 0, Nk >= 0,
  *   d in {64, 128} for bf16 and d == 128 for fp8; every tensor must hold
- *   fewer than 2^31 elements.  Nk == 0 makes every row see no key.
+ *   fewer than 2^31 elements.  Nk == 0 while B * Hq * Nq > 0 is an
+ *   FA_ERROR_INVALID_VALUE (there are rows to compute and no key).
  * causal: 0 or 1 (bottom-right aligned mask, see above).
  * scale: multiplies the raw dot products; any finite value (callers
  *   normally pass 1/sqrt(d), the formula's 1/sqrt(d_k)).

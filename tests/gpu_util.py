@@ -99,6 +99,24 @@ def sample_rows(B, Hq, Nq, seed=0, per_head=24, heads=None):
     return np.array(sorted(set(rows)), dtype=np.int64)
 
 
+def head_rows(Hq, Nq, heads):
+    """Flat row indices (b*Hq + h)*Nq + i of every row of the listed (b, h) heads."""
+    return np.concatenate([np.arange((b * Hq + h) * Nq, (b * Hq + h + 1) * Nq, dtype=np.int64)
+                           for (b, h) in heads])
+
+
+def complete_heads(B, Hq, Hkv):
+    """The (b, h) heads a full-size parity test compares row for row: the first
+    head of the first key/value group, the last head of that group (when heads
+    share keys), and the last head of the last batch entry."""
+    g = Hq // Hkv
+    heads = [(0, 0)]
+    if g > 1:
+        heads.append((0, g - 1))
+    heads.append((B - 1, Hq - 1))
+    return sorted(set(heads))
+
+
 def oracle_ref(x, dtype, causal, scale, rows=None):
     return oracle.attention(x["q"], x["k"], x["v"], causal=causal, scale=scale,
                             dtype=dtype, descale=x.get("descale"), rows=rows)

@@ -67,7 +67,8 @@ def test_valid_arguments(lib):
     assert validate(lse=None) == _lib.FA_SUCCESS
     assert validate(scale=0.0) == _lib.FA_SUCCESS
     assert validate(scale=-0.5) == _lib.FA_SUCCESS
-    assert validate(Nk=0, k=None, v=None) == _lib.FA_SUCCESS       # every row sees no key
+    assert validate(B=0, Nk=0, q=None, k=None, v=None, o=None) == _lib.FA_SUCCESS   # nothing to compute
+    assert validate(Nq=0, Nk=0, q=None, k=None, v=None, o=None, lse=None) == _lib.FA_SUCCESS
     assert validate(Nq=0, q=None, o=None, lse=None) == _lib.FA_SUCCESS
     assert validate(B=0, q=None, k=None, v=None, o=None) == _lib.FA_SUCCESS
     assert validate(dtype=_lib.FA_DTYPE_FP8_E4M3, descale=(0.01, 0.02, 0.03)) == _lib.FA_SUCCESS
@@ -84,6 +85,7 @@ def test_valid_arguments(lib):
     dict(q=None), dict(o=None), dict(k=None), dict(v=None),
     dict(q=4096 + 8), dict(k=8192 + 2), dict(o=16384 + 4), dict(lse=20480 + 2),
     dict(B=1 << 12, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 10, d=128),
+    dict(Nk=0, k=None, v=None), dict(Nk=0),                 # rows to compute, no key
 ])
 def test_invalid_arguments(lib, kw):
     assert validate(**kw) == _lib.FA_ERROR_INVALID_VALUE

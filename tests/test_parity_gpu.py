@@ -1,8 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small problems are compared element by element over the whole output; the
-full-size workloads are compared on sampled rows that the oracle computes
-one by one, plus properties that hold at any size.  Tolerances are in
+Small problems and the GPT-2-shaped and decode workloads are compared element
+by element over the whole output.  The longer full-size workloads are compared
+over complete heads (every row of the first and last head, and of the last
+head of the first key/value group under grouped-query attention) and on
+sampled rows of other heads, plus properties that hold at any size.  Tolerances are in
 gpu_util.py.
 """
 import math
@@ -12,7 +14,8 @@ import pytest
 import torch
 
 from exact_attention_105_amd import FaError, fwd
-from gpu_util import (compare_bf16, oracle_ref, run_gpu, sample_rows, say, to_device)
+from gpu_util import (compare_bf16, complete_heads, head_rows, oracle_ref, run_gpu, sample_rows, say,
+                      to_device)
 from synth.inputs import CONFIGS, generate, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -94,9 +97,14 @@ def test_no_keys_and_no_queries():
     dev = torch.device("cuda:0")
     q = torch.randn(1, 2, 5, 64, device=dev).bfloat16()
     k = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
-    o, lse = fwd(q, k, k.clone(), causal=False)
+    out = torch.full((1, 2, 5, 64), 7.0, device=dev, dtype=torch.bfloat16)
+    lse = torch.full((1, 2, 5), 7.0, device=dev)
+    # rows to compute and no key: an argument error, outputs untouched
+    with pytest.raises(FaError) as e:
+        fwd(q, k, k.clone(), causal=False, out=out, lse=lse)
+    assert e.value.status == 1
     torch.cuda.synchronize()
-    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(out == 7.0) and torch.all(lse == 7.0)
     q0 = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
     kk = torch.randn(1, 2, 7, 64, device=dev).bfloat16()
     o, lse = fwd(q0, kk, kk.clone(), causal=True)
@@ -173,6 +181,11 @@ def test_reference_moves_mid_row(shape):
 
 # ------------------------------------------------------------------ full-size workloads
 BF16_CONFIGS = ["tiny", "gpt2", "gpt2_causal", "long16k_causal", "gqa_causal", "gqa_decode"]
+# compared with the oracle over the whole output (the oracle finishes them in
+# seconds); the longer workloads are compared over complete heads -- every
+# query tile and the whole causal staircase of those heads -- plus sampled
+# rows of the other heads
+WHOLE_OUTPUT = ("tiny", "gpt2", "gpt2_causal", "gqa_decode")
 
 
 @pytest.mark.parametrize("name", BF16_CONFIGS)
@@ -183,15 +196,21 @@ def test_config_bf16(name):
     o, lse = run_gpu(x, "bf16", cfg.causal, cfg.scale)
     assert np.all(np.isfinite(o)), "unwritten or non-finite outputs"
     assert np.all(np.isfinite(lse))
-    rows_total = cfg.B * cfg.Hq * cfg.Nq
-    if rows_total <= 4096:
+    if name in WHOLE_OUTPUT:
         o_ref, lse_ref = oracle_ref(x, "bf16", cfg.causal, cfg.scale)
-        compare_bf16(o, lse, o_ref, lse_ref, name)
+        compare_bf16(o, lse, o_ref, lse_ref, f"{name} (whole output)")
     else:
-        rows = sample_rows(cfg.B, cfg.Hq, cfg.Nq, seed=cfg.seed)
+        heads = complete_heads(cfg.B, cfg.Hq, cfg.Hkv)
+        rows = head_rows(cfg.Hq, cfg.Nq, heads)
         o_ref, lse_ref = oracle_ref(x, "bf16", cfg.causal, cfg.scale, rows=rows)
         compare_bf16(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
-                     f"{name} ({rows.size} sampled rows)")
+                     f"{name} (complete heads {heads}, {rows.size} rows)")
+        others = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq) if (b, h) not in heads]
+        pick = np.random.default_rng(cfg.seed).choice(len(others), size=min(6, len(others)), replace=False)
+        rows = sample_rows(cfg.B, cfg.Hq, cfg.Nq, seed=cfg.seed, heads=[others[i] for i in sorted(pick)])
+        o_ref, lse_ref = oracle_ref(x, "bf16", cfg.causal, cfg.scale, rows=rows)
+        compare_bf16(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
+                     f"{name} ({rows.size} sampled rows of other heads)")
     if cfg.causal and cfg.Nq == cfg.Nk:
         # row 0 sees only key 0: O_0 = V_0 exactly, for every head
         from oracle_pins import bf16_to_f64_torch
@@ -241,10 +260,17 @@ def test_config_fp8():
     x = generate(cfg)
     o, lse = run_gpu(x, "e4m3", cfg.causal, cfg.scale)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    rows = sample_rows(cfg.B, cfg.Hq, cfg.Nq, seed=cfg.seed)
+    heads = complete_heads(cfg.B, cfg.Hq, cfg.Hkv)
+    rows = head_rows(cfg.Hq, cfg.Nq, heads)
     o_ref, lse_ref = oracle_ref(x, "e4m3", cfg.causal, cfg.scale, rows=rows)
     compare_fp8(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
-                f"fp8 ({rows.size} sampled rows)")
+                f"fp8 (complete heads {heads}, {rows.size} rows)")
+    others = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq) if (b, h) not in heads]
+    pick = np.random.default_rng(cfg.seed).choice(len(others), size=min(6, len(others)), replace=False)
+    rows = sample_rows(cfg.B, cfg.Hq, cfg.Nq, seed=cfg.seed, heads=[others[i] for i in sorted(pick)])
+    o_ref, lse_ref = oracle_ref(x, "e4m3", cfg.causal, cfg.scale, rows=rows)
+    compare_fp8(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
+                f"fp8 ({rows.size} sampled rows of other heads)")
 
 
 # ------------------------------------------------------------------ few query rows (decode path)

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_105_amd import default_splits, fwd, fwd_splitkv
+from exact_attention_105_amd import FaError, default_splits, fwd, fwd_splitkv
 from gpu_util import compare_bf16, say, to_device
 from synth.inputs import CONFIGS, generate, make_inputs
 
@@ -40,7 +40,6 @@ CASES = [
     (1, 16, 1, 16, 1000, False, 3),      # MQA, 256 packed rows (8 row tiles)
     (1, 8, 2, 1, 100, True, 64),         # more splits than key tiles: empty splits
     (1, 8, 2, 2, 1, False, 4),           # one key
-    (1, 8, 2, 3, 0, True, 4),            # no keys: O = 0, LSE = -inf
     (1, 32, 8, 1, 65536, True, 256),
 ]
 
@@ -54,6 +53,20 @@ def test_splitkv_matches_oracle(case):
     o, lse = run(x, causal, scale, ns)
     o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], causal=causal, scale=scale)
     compare_bf16(o, lse, o_ref, lse_ref, f"splitkv {case}")
+
+
+def test_no_keys_is_an_argument_error():
+    """Rows to compute and no key: FA_ERROR_INVALID_VALUE, outputs untouched."""
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 8, 3, 128, device=dev).bfloat16()
+    k = torch.empty(1, 2, 0, 128, device=dev, dtype=torch.bfloat16)
+    out = torch.full((1, 8, 3, 128), 7.0, device=dev, dtype=torch.bfloat16)
+    lse = torch.full((1, 8, 3), 7.0, device=dev)
+    with pytest.raises(FaError) as e:
+        fwd_splitkv(q, k, k.clone(), causal=True, scale=0.1, n_splits=4, out=out, lse=lse)
+    assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(lse == 7.0)
 
 
 def test_one_split_is_the_decode_kernel_bit_for_bit():
