@@ -9,9 +9,15 @@ N=16384, d=128, bf16, causal); ``--config`` selects another one.
 Prints one JSON line with the throughput in TFLOP/s (attention FLOPs
 4*B*Hq*Nq*Nk*d, halved for causal square problems), a ``roofline`` object
 for the kernel (MFMA-bound: achieved TFLOP/s against the dense MFMA peak of
-the input dtype; HBM-bound decode: algorithmic GB/s against 8 TB/s) and a
-``cpu_baseline`` object: the fp64 oracle timed on this host's cores on a
-bounded sample of rows of the same workload.
+the input dtype; HBM-bound decode: algorithmic GB/s against 8 TB/s; plus the
+shader clock under the kernel from the committed counter summary and the
+fraction of the peak scaled to that clock) and a ``cpu_baseline`` object: the fp64 oracle timed
+on this host's cores on a bounded sample of rows of the same workload.
+
+Timing: W untimed warm-up steps (default: back-to-back steps for 0.15 s, so
+that the GPU clock has settled), then K timed steps (default: about 0.2 s of
+steps, at least 20) between synchronisations, measured with HIP events on
+the stream the kernels run on.
 
 Other legs, each printing its own line of the same shape:
   --splitkv N       decode shapes through fa_fwd_splitkv (N key splits, 0: default)
@@ -38,7 +44,67 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}   # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s on 1 MI355X (bf16/fp8) and % of MFMA peak"
-SHORT_WORKLOADS = ("tiny", "gpt2", "gpt2_causal", "gqa_decode")
+WARM_S = 0.15     # default untimed warm-up: back-to-back steps until this much wall time has passed
+TIMED_S = 0.2     # default timed region: about this much GPU time
+
+
+def settle(step, args):
+    """Run the untimed warm-up and fix the step counts.
+
+    Without --warmup the warm-up repeats the step back to back until WARM_S
+    seconds have passed: the GPU's clock moves over the first tens of
+    milliseconds of sustained load (per-launch times on the long-context
+    workload fall by about a fifth before they level off), and the timed
+    region should see the level it settles at.  Without --steps the timed
+    region holds about TIMED_S seconds of steps (at least 20).  args.warmup and
+    args.steps are set to the counts used."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    if args.warmup is None:
+        while True:
+            for _ in range(5):
+                step()
+            n += 5
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= WARM_S:
+                break
+        args.warmup = n
+    else:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        n = args.warmup
+    per = (time.perf_counter() - t0) / max(n, 1)
+    if args.steps is None:
+        args.steps = int(min(5000, max(20, math.ceil(TIMED_S / max(per, 1e-7)))))
+
+
+def load_clock(cfg):
+    """The shader clock under the workload's kernel from the committed
+    counter summary (profiles/clock_<workload>.json: GRBM_GUI_ACTIVE / 8 XCDs
+    over the kernel's duration), if it was taken on the current kernel
+    sources; else None.  (A probe kernel launched between steps reads about
+    2.4 GHz: the clock recovers within microseconds once the load stops, so
+    only counters taken during the kernel see its clock.)"""
+    path = os.path.join(ROOT, "profiles", f"clock_{cfg.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash(cfg):
+        return None
+    return t.get("clock_mhz")
+
+
+def clock_fields(mhz, achieved, peak):
+    """The shader clock (MHz, or None) and the fraction of the peak scaled to
+    it (the published peaks are at the 2.4 GHz nameplate clock)."""
+    if mhz is None:
+        return {"clock_mhz": None}
+    peak_at = peak * mhz / 2400.0
+    return {"clock_mhz": mhz, "clock_source": "counters (profiles/clock_<workload>.json)",
+            "peak_at_clock": peak_at, "frac_at_clock": achieved / peak_at}
 
 
 def kernel_source(cfg) -> str:
@@ -256,9 +322,7 @@ def rotate_bench(args):
     codes = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev)
     scale = torch.empty(1, dtype=torch.float32, device=dev)
     work = torch.empty(1, dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
-        rotate_quantize(x, signs=signs, codes=codes, scale=scale, work=work)
-    torch.cuda.synchronize()
+    settle(lambda: rotate_quantize(x, signs=signs, codes=codes, scale=scale, work=work), args)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -322,9 +386,7 @@ def bwd_bench(args):
     def step():
         bwd(q, k, v, o, lse, do, causal=cfg.causal, scale=cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    settle(step, args)
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -389,9 +451,13 @@ def varlen_bench(args):
     lse = torch.empty((w["Hq"], q.shape[0]), dtype=torch.float32, device=dev)
 
     def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        if steps is None or warmup is None:
+            settle(fn, args)
+            steps = args.steps
+        else:
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
         stream = torch.cuda.current_stream(dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -440,7 +506,7 @@ def varlen_bench(args):
     qp = torch.zeros((B, w["Hq"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
     kp = torch.zeros((B, w["Hkv"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
     vp = torch.zeros_like(kp)
-    ms_pad = timed(lambda: fwd(qp, kp, vp, causal=w["causal"], scale=scale), max(1, args.steps // 2), 1)
+    ms_pad = timed(lambda: fwd(qp, kp, vp, causal=w["causal"], scale=scale), max(1, args.steps // 2), 3)
     del qp, kp, vp
     cpu = None
     if args.cpu_budget > 0:
@@ -577,9 +643,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; 200 for the short workloads tiny, gpt2, gpt2_causal "
-                         "and gqa_decode, whose launches last tens to hundreds of microseconds)")
-    ap.add_argument("--warmup", type=int, default=5)
+                    help=f"timed steps (default: about {TIMED_S} s of steps, at least 20)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help=f"untimed warm-up steps (default: back-to-back steps for {WARM_S} s, until the "
+                         "GPU clock has settled)")
     ap.add_argument("--config", default="long16k_causal")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 to skip)")
@@ -599,9 +666,9 @@ def main():
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
     args = ap.parse_args()
-    if args.steps is None:
-        short = not (args.varlen or args.bwd or args.rotate or args.gemm_reference or args.copy_bytes)
-        args.steps = 200 if short and args.config in SHORT_WORKLOADS else 20
+    if args.copy_bytes > 0 or args.gemm_reference > 0:
+        args.warmup = 5 if args.warmup is None else args.warmup
+        args.steps = 20 if args.steps is None else args.steps
     if args.copy_bytes > 0:
         copy_calibration(args)
         return
@@ -653,9 +720,7 @@ def main():
         def step():
             fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, descale=descale, out=out, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    settle(step, args)
     stream = torch.cuda.current_stream(dev)
     # one event between consecutive launches: the first-to-last span gives the
     # whole-job time, the gaps give per-launch median and minimum
@@ -700,6 +765,7 @@ def main():
         peak = PEAK_TFLOPS[cfg.dtype]
         roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": tflops / peak}
+    roof.update(clock_fields(None if n_splits else load_clock(cfg), roof["achieved"], roof["peak"]))
     roof["traffic"] = load_traffic(cfg, "_splitkv" if n_splits else "")
     roof["kernel_ms"] = ms
     roof["kernel_ms_median"] = ms_median

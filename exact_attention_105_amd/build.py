@@ -71,6 +71,29 @@ def build(verbose: bool = False, jobs: int = 4, extra_flags=(), out: str = LIB,
     return out
 
 
+MICROBENCH = os.path.join(PKG, "microbench")
+MICROBENCH_SOURCES = ["issue_rates.hip", "fp8_accumulation.hip"]
+
+
+def build_microbench(verbose: bool = False) -> list:
+    """Compile the stand-alone microbenchmark programs (microbench/*.hip)
+    into microbench/bin/; returns their paths."""
+    cc = hipcc()
+    outdir = os.path.join(MICROBENCH, "bin")
+    os.makedirs(outdir, exist_ok=True)
+    procs, outs = [], []
+    for src in MICROBENCH_SOURCES:
+        out = os.path.join(outdir, src.replace(".hip", ""))
+        outs.append(out)
+        cmd = [cc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", os.path.join(MICROBENCH, src), "-o", out]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    _drain(procs)
+    return outs
+
+
 def _drain(procs):
     failed = []
     for src, pr in procs:
@@ -86,3 +109,4 @@ def _drain(procs):
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_microbench(verbose=True))

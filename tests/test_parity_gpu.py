@@ -233,28 +233,28 @@ FP8_SMALL = [
 @pytest.mark.parametrize("shape", FP8_SMALL, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}Nq{s[3]}Nk{s[4]}{'c' if s[5] else 'n'}"
                                                   for s in FP8_SMALL])
 def test_small_fp8(shape):
-    from gpu_util import compare_fp8
+    from gpu_util import compare_fp8, fp8_lse_bound
     B, Hq, Hkv, Nq, Nk, causal = shape
     say(f"fp8 case {shape}")
     x = make_inputs(B, Hq, Hkv, Nq, Nk, 128, "e4m3", 2000 + sum(shape))
     scale = 1.0 / math.sqrt(128)
     o, lse = run_gpu(x, "e4m3", causal, scale)
     o_ref, lse_ref = oracle_ref(x, "e4m3", causal, scale)
-    compare_fp8(o, lse, o_ref, lse_ref, f"fp8 {shape}")
+    compare_fp8(o, lse, o_ref, lse_ref, f"fp8 {shape}", lse_bound=fp8_lse_bound(x, None, scale))
     # rows without any visible key follow the convention exactly
     assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref))
 
 
 def test_fp8_negative_scale():
-    from gpu_util import compare_fp8
+    from gpu_util import compare_fp8, fp8_lse_bound
     x = make_inputs(1, 2, 2, 150, 150, 128, "e4m3", 2100)
     o, lse = run_gpu(x, "e4m3", True, -0.05)
     o_ref, lse_ref = oracle_ref(x, "e4m3", True, -0.05)
-    compare_fp8(o, lse, o_ref, lse_ref, "fp8 scale=-0.05")
+    compare_fp8(o, lse, o_ref, lse_ref, "fp8 scale=-0.05", lse_bound=fp8_lse_bound(x, None, -0.05))
 
 
 def test_config_fp8():
-    from gpu_util import compare_fp8
+    from gpu_util import compare_fp8, fp8_lse_bound
     cfg = CONFIGS["fp8"]
     say(f"config fp8: {cfg}")
     x = generate(cfg)
@@ -264,13 +264,13 @@ def test_config_fp8():
     rows = head_rows(cfg.Hq, cfg.Nq, heads)
     o_ref, lse_ref = oracle_ref(x, "e4m3", cfg.causal, cfg.scale, rows=rows)
     compare_fp8(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
-                f"fp8 (complete heads {heads}, {rows.size} rows)")
+                f"fp8 (complete heads {heads}, {rows.size} rows)", lse_bound=fp8_lse_bound(x, rows, cfg.scale))
     others = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq) if (b, h) not in heads]
     pick = np.random.default_rng(cfg.seed).choice(len(others), size=min(6, len(others)), replace=False)
     rows = sample_rows(cfg.B, cfg.Hq, cfg.Nq, seed=cfg.seed, heads=[others[i] for i in sorted(pick)])
     o_ref, lse_ref = oracle_ref(x, "e4m3", cfg.causal, cfg.scale, rows=rows)
     compare_fp8(o.reshape(-1, cfg.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref,
-                f"fp8 ({rows.size} sampled rows of other heads)")
+                f"fp8 ({rows.size} sampled rows of other heads)", lse_bound=fp8_lse_bound(x, rows, cfg.scale))
 
 
 # ------------------------------------------------------------------ few query rows (decode path)

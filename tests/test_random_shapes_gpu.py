@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from exact_attention_105_amd import fwd_splitkv
-from gpu_util import compare_bf16, compare_fp8, oracle_ref, run_gpu, say, to_device
+from gpu_util import compare_bf16, compare_fp8, fp8_lse_bound, oracle_ref, run_gpu, say, to_device
 from synth.inputs import make_grad_output, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -66,7 +66,7 @@ def test_random_forward_fp8(case):
     scale = smul / math.sqrt(d)
     o, lse = run_gpu(x, "e4m3", causal, scale)
     o_ref, lse_ref = oracle_ref(x, "e4m3", causal, scale)
-    compare_fp8(o, lse, o_ref, lse_ref, str(case))
+    compare_fp8(o, lse, o_ref, lse_ref, str(case), lse_bound=fp8_lse_bound(x, None, scale))
 
 
 def _draw_decode(n, seed):
