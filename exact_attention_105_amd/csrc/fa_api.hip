@@ -170,6 +170,7 @@ extern "C" fa_status_t fa_bwd_validate(const void* q, const void* k, const void*
     const int64_t kv_elems = (int64_t)B * Hkv * Nk * d;
     if (q_elems > kMaxElems || kv_elems > kMaxElems) return FA_ERROR_INVALID_VALUE;
     if (q_elems > 0) {
+        if (Nk == 0) return FA_ERROR_INVALID_VALUE;   // rows to differentiate and no key, as in fa_fwd
         if (q == nullptr || o == nullptr || dout == nullptr || dq == nullptr || lse == nullptr ||
             workspace == nullptr)
             return FA_ERROR_INVALID_VALUE;

@@ -227,7 +227,8 @@ fa_status_t fa_fwd_splitkv_validate(const void* q, const void* k, const void* v,
  *   workspace        2 * B * Hq * Nq floats the call overwrites (D and a
  *                    base-2 copy of lse); calls that share it must be ordered
  * dq, dk and dv are written in full (keys no query sees get zero gradients).
- * dtype must be FA_DTYPE_BF16; d in {64, 128}; other sizes as in fa_fwd.
+ * dtype must be FA_DTYPE_BF16; d in {64, 128}; other sizes as in fa_fwd
+ * (Nk == 0 while B * Hq * Nq > 0 is an FA_ERROR_INVALID_VALUE, as there).
  *
  * Returns FA_SUCCESS once the kernels are enqueued, FA_ERROR_INVALID_VALUE
  * for a null or misaligned pointer or an out-of-range size,

@@ -155,8 +155,10 @@ def test_bwd_valid_arguments(lib):
     assert bvalidate(scale=-0.5) == _lib.FA_SUCCESS
     # no query rows: the query-side pointers may be null
     assert bvalidate(Nq=0, q=None, o=None, lse=None, do=None, dq=None, ws=None) == _lib.FA_SUCCESS
-    # no keys: the key-side pointers may be null
-    assert bvalidate(Nk=0, k=None, v=None, dk=None, dv=None) == _lib.FA_SUCCESS
+    # no query rows and no keys: nothing to compute, every pointer may be null
+    assert bvalidate(Nq=0, Nk=0, q=None, o=None, lse=None, do=None, dq=None, ws=None,
+                     k=None, v=None, dk=None, dv=None) == _lib.FA_SUCCESS
+    assert bvalidate(B=0, Nk=0) == _lib.FA_SUCCESS
 
 
 @pytest.mark.parametrize("kw", [
@@ -167,6 +169,7 @@ def test_bwd_valid_arguments(lib):
     dict(q=4096 + 8), dict(do=24576 + 2), dict(dq=28672 + 4), dict(dk=32768 + 8), dict(dv=36864 + 1),
     dict(lse=20480 + 2), dict(ws=40960 + 1),
     dict(B=1, Hq=1, Hkv=1, Nq=1 << 24, d=128),
+    dict(Nk=0), dict(Nk=0, k=None, v=None, dk=None, dv=None),   # rows to differentiate and no key
 ])
 def test_bwd_invalid_arguments(lib, kw):
     assert bvalidate(**kw) == _lib.FA_ERROR_INVALID_VALUE

@@ -22,7 +22,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_105_amd import bwd, fwd
+from exact_attention_105_amd import FaError, bwd, fwd
 from gpu_util import say
 from synth.inputs import CONFIGS, make_grad_output, make_inputs
 
@@ -113,13 +113,29 @@ def test_backward_matches_oracle(case):
 
 
 def test_backward_empty_sides():
-    # no query rows: dK = dV = 0; no keys: dQ = 0
-    for (Nq, Nk) in ((0, 50), (40, 0)):
-        x = make_inputs(1, 2, 2, Nq, Nk, 128, "bf16", 99)
-        do_bits = make_grad_output(1, 2, Nq, 128, 99)
-        say(f"backward Nq={Nq} Nk={Nk}")
-        dq, dk, dv = run(x, do_bits, True, 0.1)
-        assert not dq.any() and not dk.any() and not dv.any()
+    # no query rows: dK = dV = 0
+    x = make_inputs(1, 2, 2, 0, 50, 128, "bf16", 99)
+    do_bits = make_grad_output(1, 2, 0, 128, 99)
+    say("backward Nq=0 Nk=50")
+    dq, dk, dv = run(x, do_bits, True, 0.1)
+    assert not dq.any() and not dk.any() and not dv.any()
+
+
+def test_backward_no_keys_is_an_argument_error():
+    """Query rows and no key: FA_ERROR_INVALID_VALUE (as for the forward),
+    nothing launched, the gradients untouched."""
+    dev = torch.device("cuda:0")
+    q = torch.zeros((1, 2, 40, 128), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device=dev)
+    o = torch.zeros_like(q)
+    lse = torch.zeros((1, 2, 40), dtype=torch.float32, device=dev)
+    dq = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    say("backward Nq=40 Nk=0")
+    with pytest.raises(FaError) as e:
+        bwd(q, k, k.clone(), o, lse, o.clone(), causal=True, scale=0.1, dq=dq)
+    assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert torch.isnan(dq.float()).all()
 
 
 def test_backward_full_size_long_context():
