@@ -13,5 +13,5 @@ the FP8 kernel.  The C ABI is declared in include/fa.h; ``_lib`` is its
 ctypes binding.
 """
 from ._lib import EXPORTED, FaError, load, status_string, version  # noqa: F401
-from .attention import (bwd, bwd_varlen, default_splits, fwd, fwd_splitkv, fwd_varlen,  # noqa: F401
-                        rotate_quantize, sign_bits)
+from .attention import (bwd, bwd_varlen, default_splits, fwd, fwd_splitkv, fwd_splitkv_noalloc,  # noqa: F401
+                        fwd_varlen, rotate_quantize, sign_bits)

@@ -20,10 +20,11 @@ FA_SUCCESS = 0
 FA_ERROR_INVALID_VALUE = 1
 FA_ERROR_NOT_SUPPORTED = 2
 FA_ERROR_LAUNCH_FAILURE = 3
+SPLITKV_SCRATCH_FLOATS = 4 << 20   # FA_SPLITKV_SCRATCH_FLOATS in include/fa.h
 
 # every symbol include/fa.h declares
 EXPORTED = ("fa_fwd", "fa_fwd_validate", "fa_fwd_varlen", "fa_fwd_varlen_validate", "fa_fwd_splitkv",
-            "fa_fwd_splitkv_validate", "fa_bwd", "fa_bwd_validate", "fa_bwd_varlen", "fa_bwd_varlen_validate",
+            "fa_fwd_splitkv_validate", "fa_fwd_splitkv_noalloc", "fa_bwd", "fa_bwd_validate", "fa_bwd_varlen", "fa_bwd_varlen_validate",
             "fa_rotate_quantize_e4m3", "fa_rotate_quantize_validate", "fa_status_string", "fa_version")
 
 _lib = None
@@ -58,6 +59,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_splitkv.restype = i32
     lib.fa_fwd_splitkv.argtypes = [vp] * 5 + [i32] * 7 + [f32, i32, i32, vp, vp]
     lib.fa_fwd_splitkv_validate.restype = i32
+    lib.fa_fwd_splitkv_noalloc.restype = i32
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp] * 5 + [i32] * 7 + [f32, i32, i32, vp]
     lib.fa_fwd_splitkv_validate.argtypes = [vp] * 5 + [i32] * 7 + [f32, i32, i32, vp]
     lib.fa_fwd_varlen.restype = i32
     lib.fa_fwd_varlen.argtypes = [vp] * 7 + [i32] * 8 + [f32, i32, vp]
@@ -111,6 +114,14 @@ def fa_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, c
     """Raw call of fa_fwd_splitkv with integer device pointers; returns the status code."""
     return load().fa_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, int(causal),
                                  float(scale), int(dtype), int(n_splits), ws_ptr, stream)
+
+
+def fa_fwd_splitkv_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype,
+                           n_splits, stream) -> int:
+    """Raw call of fa_fwd_splitkv_noalloc (the library's own scratch array
+    instead of a workspace); returns the status code."""
+    return load().fa_fwd_splitkv_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, int(causal),
+                                         float(scale), int(dtype), int(n_splits), stream)
 
 
 def fa_fwd_splitkv_validate(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype,

@@ -93,13 +93,8 @@ def default_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int) -> int:
     return int(max(1, min(256, -(-128 // max(units, 1)), Nk // 4096)))
 
 
-def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
-                scale: float | None = None, n_splits: int | None = None, workspace: torch.Tensor | None = None,
-                out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """Decode-shaped attention (bf16, d = 128, Nq <= 16) with the keys split
-    over ``n_splits`` workgroups per key/value head and merged afterwards;
-    returns (O, LSE) like ``fwd``.  ``n_splits`` defaults to
-    ``default_splits``; ``workspace`` holds n_splits*B*Hq*Nq*(d+1) floats."""
+def _splitkv_args(q, k, v, causal, scale, n_splits, out, lse):
+    """Checks and defaults shared by fwd_splitkv and fwd_splitkv_noalloc."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or t.dim() != 4 or not t.is_contiguous() or t.dtype != torch.bfloat16:
             raise ValueError(f"{name} must be a contiguous bfloat16 [B, H, N, d] GPU tensor")
@@ -113,12 +108,24 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
         n_splits = default_splits(B, Hq, Hkv, Nq, Nk)
     if out is None:
         out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
-    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, Hq, Nq, d):
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, Hq, Nq, d) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 [B, Hq, Nq, d] tensor")
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq):
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    return (B, Hq, Hkv, Nq, Nk, d), float(scale), int(n_splits), out, lse
+
+
+def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                scale: float | None = None, n_splits: int | None = None, workspace: torch.Tensor | None = None,
+                out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Decode-shaped attention (bf16, d = 128, Nq <= 16) with the keys split
+    over ``n_splits`` workgroups per key/value head and merged afterwards;
+    returns (O, LSE) like ``fwd``.  ``n_splits`` defaults to
+    ``default_splits``; ``workspace`` holds n_splits*B*Hq*Nq*(d+1) floats."""
+    dims, scale, n_splits, out, lse = _splitkv_args(q, k, v, causal, scale, n_splits, out, lse)
+    B, Hq, Hkv, Nq, Nk, d = dims
     need = n_splits * B * Hq * Nq * (d + 1)
     if workspace is None and n_splits > 1:
         workspace = torch.empty(max(need, 1), dtype=torch.float32, device=q.device)
@@ -129,6 +136,26 @@ def fwd_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
     st = _lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                              B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale, _lib.FA_DTYPE_BF16, n_splits,
                              workspace.data_ptr() if workspace is not None else None, stream)
+    if st != _lib.FA_SUCCESS:
+        raise _lib.FaError(st, _lib.status_string(st))
+    return out, lse
+
+
+def fwd_splitkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, out: torch.Tensor,
+                        lse: torch.Tensor, causal: bool = False, scale: float | None = None,
+                        n_splits: int | None = None):
+    """``fwd_splitkv`` without a workspace: the split partials go to the
+    library's own scratch array on each GPU (``_lib.SPLITKV_SCRATCH_FLOATS``
+    floats; larger problems raise FaError).  The caller passes ``out`` and
+    ``lse``, so the call allocates nothing.  Calls that overlap on one GPU
+    share that array and race: order them on one stream."""
+    dims, scale, n_splits, out, lse = _splitkv_args(q, k, v, causal, scale, n_splits, out, lse)
+    B, Hq, Hkv, Nq, Nk, d = dims
+    _on_device(q.device, k=k, v=v, out=out, lse=lse)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _lib.fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                     B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale, _lib.FA_DTYPE_BF16,
+                                     n_splits, stream)
     if st != _lib.FA_SUCCESS:
         raise _lib.FaError(st, _lib.status_string(st))
     return out, lse

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_bwd.hpp"
 #include "fa_launch.hpp"
@@ -14,6 +16,34 @@ namespace {
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace
+
+// Split-KV partials for fa_fwd_splitkv_noalloc: one copy per GPU, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// the device array: host code only ever uses the address that
+// hipGetSymbolAddress returns for the current device (scratch_on_device).
+static __device__ __align__(256) float scratch[FA_SPLITKV_SCRATCH_FLOATS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device with
+// that device current; nullptr if the lookup fails.
+float* scratch_on_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        g_scratch_ptr[dev] = static_cast<float*>(ptr);
+    }
+    return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -338,6 +368,29 @@ extern "C" fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* 
     p.q_sign = scale < 0.f ? 0x80008000u : 0u;
     const hipError_t err = fa::launch_fwd_decode_split(p, causal != 0, n_splits, workspace, stream);
     return err == hipSuccess ? FA_SUCCESS : FA_ERROR_LAUNCH_FAILURE;
+}
+
+extern "C" fa_status_t fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                              int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                                              float scale, fa_dtype_t dtype, int n_splits, hipStream_t stream) {
+    // Argument checks with a stand-in workspace pointer (aligned, non-null);
+    // the real one is looked up only for a call that launches.
+    static float stand_in[4] __attribute__((aligned(16)));
+    fa_status_t st = fa_fwd_splitkv_validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype,
+                                             n_splits, stand_in);
+    if (st != FA_SUCCESS) return st;
+    const int64_t rows = (int64_t)B * Hq * Nq;
+    if (n_splits > 1 && rows * n_splits * (int64_t)(d + 1) > (int64_t)FA_SPLITKV_SCRATCH_FLOATS)
+        return FA_ERROR_INVALID_VALUE;
+    if (rows == 0) return FA_SUCCESS;
+    float* ws = nullptr;
+    if (n_splits > 1) {
+        ws = scratch_on_device();
+        if (ws == nullptr) return FA_ERROR_LAUNCH_FAILURE;
+    }
+    // Every split writes its whole partial (O and LSE) before the merge reads
+    // it, so nothing in the scratch has to start at zero.
+    return fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, dtype, n_splits, ws, stream);
 }
 
 extern "C" fa_status_t fa_bwd_varlen_validate(const void* q, const void* k, const void* v, const void* o,

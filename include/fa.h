@@ -206,6 +206,30 @@ fa_status_t fa_fwd_splitkv_validate(const void* q, const void* k, const void* v,
                                     const float* workspace);
 
 /*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, hosts that forbid allocation.
+ *
+ * The split partials go to a scratch array of FA_SPLITKV_SCRATCH_FLOATS
+ * floats (16 MiB) that the library holds in each GPU's memory from load until
+ * the process ends; the call allocates nothing (no hipMalloc, no allocating
+ * library routine).  Arguments and result as fa_fwd_splitkv; a call with
+ * n_splits > 1 whose n_splits * B * Hq * Nq * (d + 1) floats exceed
+ * FA_SPLITKV_SCRATCH_FLOATS returns FA_ERROR_INVALID_VALUE before any launch
+ * (n_splits = 1 uses no scratch), and one whose scratch array cannot be
+ * located on the current device FA_ERROR_LAUNCH_FAILURE.  The scratch array
+ * keeps the last call's contents (every split overwrites its partial before
+ * the merge reads it).  All calls on one GPU share its array: calls that
+ * overlap in time on one GPU (on different streams, or from several host
+ * threads without ordering) race and give wrong results; order them on one
+ * stream.
+ */
+#define FA_SPLITKV_SCRATCH_FLOATS (4u << 20)
+fa_status_t fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                   int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                                   fa_dtype_t dtype, int n_splits, hipStream_t stream);
+
+/*
  * fa_bwd -- backward pass of fa_fwd (bf16), asynchronous on `stream`.
  *
  * Given the forward inputs q, k, v, the forward outputs o and lse (as

@@ -250,6 +250,35 @@ def test_splitkv_unsupported(lib, kw):
     assert svalidate(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
 
 
+def noalloc(**kw):
+    """fa_fwd_splitkv_noalloc on arguments it rejects before any HIP call
+    (fake device pointers, null stream): nothing is launched."""
+    a = dict(SGOOD)
+    a.update(kw)
+    return _lib.fa_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                       a["Nk"], a["d"], a["causal"], a["scale"], a["dtype"], a["n_splits"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(n_splits=0), dict(q=None), dict(Hkv=3), dict(scale=math.nan),
+                                dict(B=64, Nq=16, n_splits=256),
+                                dict(B=32, Nq=2, n_splits=16)])     # 16*32*32*2*129 floats > 4 Mi
+def test_splitkv_noalloc_invalid_arguments(lib, kw):
+    assert noalloc(**kw) == _lib.FA_ERROR_INVALID_VALUE
+
+
+def test_splitkv_noalloc_scratch_limit_is_the_header_constant():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    m = re.search(r"#define FA_SPLITKV_SCRATCH_FLOATS \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.SPLITKV_SCRATCH_FLOATS
+    # largest accepted problem at 16 splits, d = 128: 16 * 2032 rows * 129 floats
+    assert 16 * 2032 * 129 <= _lib.SPLITKV_SCRATCH_FLOATS < 16 * 2033 * 129
+
+
+@pytest.mark.parametrize("kw", [dict(d=64), dict(Nq=17), dict(dtype=_lib.FA_DTYPE_FP8_E4M3)])
+def test_splitkv_noalloc_unsupported(lib, kw):
+    assert noalloc(**kw) == _lib.FA_ERROR_NOT_SUPPORTED
+
+
 # ---------------------------------------------------------------- fa_bwd_varlen
 BVGOOD = dict(q=4096, k=8192, v=12288, o=16384, lse=20480, do=24576, dq=28672, dk=32768, dv=36864, ws=40960,
               cuq=45056, cuk=49152, n_seqs=3, max_q=700, max_k=800, total_q=1000, total_k=1200, Hq=8, Hkv=2,
