@@ -14,10 +14,11 @@ shader clock under the kernel from the committed counter summary and the
 fraction of the peak scaled to that clock) and a ``cpu_baseline`` object: the fp64 oracle timed
 on this host's cores on a bounded sample of rows of the same workload.
 
-Timing: W untimed warm-up steps (default: back-to-back steps for 0.15 s, so
-that the GPU clock has settled), then K timed steps (default: about 0.2 s of
-steps, at least 20) between synchronisations, measured with HIP events on
-the stream the kernels run on.
+Timing: back-to-back untimed steps for 0.15 s (settle_steps; the GPU clock
+dips under the sudden load and recovers over 20-30 launches of the
+long-context workload), then W untimed warm-up steps (default 5), then K
+timed steps (default: about 0.2 s of steps, at least 20) between
+synchronisations, measured with HIP events on the stream the kernels run on.
 
 Other legs, each printing its own line of the same shape:
   --splitkv N       decode shapes through fa_fwd_splitkv (N key splits, 0: default)
@@ -44,38 +45,41 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}   # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd TFLOP/s on 1 MI355X (bf16/fp8) and % of MFMA peak"
-WARM_S = 0.15     # default untimed warm-up: back-to-back steps until this much wall time has passed
+SETTLE_S = 0.15   # default clock-settling phase before the warm-up steps: back-to-back steps for this long
+WARMUP = 5        # default untimed warm-up steps after it
 TIMED_S = 0.2     # default timed region: about this much GPU time
 
 
 def settle(step, args):
-    """Run the untimed warm-up and fix the step counts.
+    """Bring the GPU to its sustained clock, run the W untimed warm-up steps
+    and fix the timed step count.
 
-    Without --warmup the warm-up repeats the step back to back until WARM_S
-    seconds have passed: the GPU's clock moves over the first tens of
-    milliseconds of sustained load (per-launch times on the long-context
-    workload fall by about a fifth before they level off), and the timed
-    region should see the level it settles at.  Without --steps the timed
-    region holds about TIMED_S seconds of steps (at least 20).  args.warmup and
-    args.steps are set to the counts used."""
+    Before the W warm-up steps (--warmup) the step runs back to back for
+    --settle-s seconds (default SETTLE_S; 0 skips this).  Under a sudden
+    sustained load the GPU's power management first pulls the clock down
+    (on the long-context workload from about 1.52 GHz on the first launch to
+    1.24 GHz on the third) and lets it recover over the next 20-30 launches
+    to the level it then holds (about 1.55 GHz); per-launch times fall by
+    about a fifth meanwhile.  The timed region should see that sustained
+    level, so these launches come first; they are reported as settle_steps.
+    Without --steps the timed region holds about TIMED_S seconds of steps
+    (at least 20).  args.settle_steps and args.steps are set to the counts used."""
     import torch
     t0 = time.perf_counter()
     n = 0
-    if args.warmup is None:
+    if args.settle_s > 0:
         while True:
             for _ in range(5):
                 step()
             n += 5
             torch.cuda.synchronize()
-            if time.perf_counter() - t0 >= WARM_S:
+            if time.perf_counter() - t0 >= args.settle_s:
                 break
-        args.warmup = n
-    else:
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        n = args.warmup
-    per = (time.perf_counter() - t0) / max(n, 1)
+    args.settle_steps = n
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per = (time.perf_counter() - t0) / max(n + args.warmup, 1)
     if args.steps is None:
         args.steps = int(min(5000, max(20, math.ceil(TIMED_S / max(per, 1e-7)))))
 
@@ -348,7 +352,8 @@ def rotate_bench(args):
         cpu = {"value": v, "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(), "sample": sample}
     del qf
     print(json.dumps({"metric": "rotate+quantize E4M3 GB/s (algorithmic) on 1 MI355X", "value": gbs,
-                      "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+                      "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "settle_steps": args.settle_steps, "ms_per_step": ms,
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
                       "data": "synthetic",
                       "config": {"workload": "fp8 query tensor rotate+quantize", "rows": n // cfg.d, "d": cfg.d,
@@ -404,7 +409,8 @@ def bwd_bench(args):
         cpu = bwd_cpu_baseline(cfg, x, dob, args.cpu_budget)
     print(json.dumps({
         "metric": "attention backward TFLOP/s (2.5x forward FLOPs) on 1 MI355X", "value": tflops,
-        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": args.settle_steps,
+        "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs and dO)",
         "config": {"workload": cfg.name + " backward", "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Nq": cfg.Nq,
@@ -450,8 +456,8 @@ def varlen_bench(args):
     out = torch.empty_like(q)
     lse = torch.empty((w["Hq"], q.shape[0]), dtype=torch.float32, device=dev)
 
-    def timed(fn, steps, warmup):
-        if steps is None or warmup is None:
+    def timed(fn, steps, warmup, settle_first=True):
+        if settle_first:
             settle(fn, args)
             steps = args.steps
         else:
@@ -488,7 +494,8 @@ def varlen_bench(args):
             cpu = varlen_bwd_cpu_baseline(x, dob, lens, w, scale, args.cpu_budget)
         print(json.dumps({
             "metric": "varlen attention backward TFLOP/s (2.5x forward FLOPs) on 1 MI355X", "value": tflops,
-            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "settle_steps": args.settle_steps, "ms_per_step": ms,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) inputs and dO)",
             "config": {"workload": args.varlen + " backward", "n_seqs": int(len(lens)), "total_tokens": int(L.sum()),
@@ -506,7 +513,8 @@ def varlen_bench(args):
     qp = torch.zeros((B, w["Hq"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
     kp = torch.zeros((B, w["Hkv"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
     vp = torch.zeros_like(kp)
-    ms_pad = timed(lambda: fwd(qp, kp, vp, causal=w["causal"], scale=scale), max(1, args.steps // 2), 3)
+    ms_pad = timed(lambda: fwd(qp, kp, vp, causal=w["causal"], scale=scale), max(1, args.steps // 2), 3,
+                   settle_first=False)
     del qp, kp, vp
     cpu = None
     if args.cpu_budget > 0:
@@ -514,7 +522,8 @@ def varlen_bench(args):
     peak = PEAK_TFLOPS["bf16"]
     print(json.dumps({
         "metric": "varlen attention forward TFLOP/s on 1 MI355X", "value": tflops, "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": args.settle_steps,
+        "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": args.varlen, "n_seqs": int(B), "total_tokens": int(L.sum()), "max_seqlen": maxlen,
                    "Hq": w["Hq"], "Hkv": w["Hkv"], "d": w["d"], "causal": w["causal"], "flops_per_step": flops,
@@ -645,8 +654,10 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help=f"timed steps (default: about {TIMED_S} s of steps, at least 20)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help=f"untimed warm-up steps (default: back-to-back steps for {WARM_S} s, until the "
-                         "GPU clock has settled)")
+                    help=f"untimed warm-up steps after the clock-settling phase (default {WARMUP})")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of back-to-back untimed steps before the warm-up steps, so that the GPU "
+                         "clock has reached its sustained level (0: none)")
     ap.add_argument("--config", default="long16k_causal")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 to skip)")
@@ -666,6 +677,7 @@ def main():
                     help="instead of attention, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
     args = ap.parse_args()
+    args.settle_steps = 0
     if args.copy_bytes > 0 or args.gemm_reference > 0:
         args.warmup = 5 if args.warmup is None else args.warmup
         args.steps = 20 if args.steps is None else args.steps
@@ -675,6 +687,7 @@ def main():
     if args.gemm_reference > 0:
         gemm_reference(args)
         return
+    args.warmup = WARMUP if args.warmup is None else args.warmup
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -775,7 +788,7 @@ def main():
 
     result = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": args.settle_steps, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Nq": cfg.Nq,
