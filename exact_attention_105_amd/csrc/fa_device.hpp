@@ -197,8 +197,11 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 // through M0).  Issued as inline asm so the compiler does not order later LDS
 // reads behind it; completion is awaited explicitly (vmcnt) before the
 // barrier that publishes a tile.  M0 is listed as clobbered; clang warns about
-// clobbering a reserved register, but no other code in these kernels keeps a
-// value in M0 (checked in the ISA).
+// clobbering a reserved register, so correctness rests on the compiler keeping
+// no value of its own in M0 across these copies.  tests/test_m0_isa.py checks
+// that on the generated assembly of every kernel that uses dma16 (clang's
+// __builtin_amdgcn_global_load_lds, which manages M0 itself, makes the
+// compiler wait for the copies in flight before the V^T reads: 9-15 % slower).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const char* gbase, uint32_t voff, uint32_t lds) {
