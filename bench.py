@@ -131,14 +131,15 @@ def _code_only(text: bytes) -> bytes:
 
 
 def kernel_source_hash(cfg) -> str:
-    """Hash of what the workload's kernel is compiled from: its source file
-    and the shared device header (code only, comments ignored) and that
-    file's extra compiler flags."""
+    """Hash of what the workload's kernel is compiled from: its source file,
+    the shared device header (and, for the bf16 prefill kernel, the
+    variable-length header it includes), code only, comments ignored, and
+    that file's extra compiler flags."""
     from exact_attention_105_amd import build as _build
     src = kernel_source(cfg)
     csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
     h = hashlib.sha256()
-    for f in (src, "fa_device.hpp"):
+    for f in (src, "fa_device.hpp") + (("fa_varlen.hpp",) if src == "fa_fwd_bf16.hip" else ()):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + _code_only(fh.read()))
     h.update(" ".join(_build.HIPCC_FLAGS + _build.SOURCE_FLAGS.get(src, [])).encode())
@@ -440,11 +441,11 @@ def varlen_bench(args):
     beside it (padded_batch_ms)."""
     import torch
     from exact_attention_105_amd import fwd, fwd_varlen, load
-    from synth.inputs import VARLEN_WORKLOADS, make_varlen_inputs, varlen_lengths
+    from synth.inputs import VARLEN_WORKLOADS, make_varlen_inputs, workload_lengths
 
     load()
     w = VARLEN_WORKLOADS[args.varlen]
-    lens = varlen_lengths(w["n_seqs"], w["lo"], w["hi"], w["seed"])
+    lens = workload_lengths(w)
     x = make_varlen_inputs(lens, lens, w["Hq"], w["Hkv"], w["d"], w["seed"])
     dev = torch.device("cuda:0")
     conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -508,14 +509,17 @@ def varlen_bench(args):
     ms = timed(lambda: fwd_varlen(q, k, v, cq, ck, maxlen, causal=w["causal"], scale=scale, out=out, lse=lse),
                args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
-    # the same sequences, zero-padded to the longest, through the fixed-length kernel
+    # the same sequences, zero-padded to the longest, through the fixed-length
+    # kernel (when the padded tensors stay within its 2^31-element limit)
     B = len(lens)
-    qp = torch.zeros((B, w["Hq"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
-    kp = torch.zeros((B, w["Hkv"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
-    vp = torch.zeros_like(kp)
-    ms_pad = timed(lambda: fwd(qp, kp, vp, causal=w["causal"], scale=scale), max(1, args.steps // 2), 3,
-                   settle_first=False)
-    del qp, kp, vp
+    ms_pad = None
+    if B * max(w["Hq"], w["Hkv"]) * maxlen * w["d"] < 2 ** 31:
+        qp = torch.zeros((B, w["Hq"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
+        kp = torch.zeros((B, w["Hkv"], maxlen, w["d"]), dtype=torch.bfloat16, device=dev)
+        vp = torch.zeros_like(kp)
+        ms_pad = timed(lambda: fwd(qp, kp, vp, causal=w["causal"], scale=scale), max(1, args.steps // 2), 3,
+                       settle_first=False)
+        del qp, kp, vp
     cpu = None
     if args.cpu_budget > 0:
         cpu = varlen_cpu_baseline(x, lens, w, scale, args.cpu_budget)

@@ -39,6 +39,7 @@
 
 #include "fa_bwd.hpp"
 #include "fa_device.hpp"
+#include "fa_varlen.hpp"
 
 
 namespace fa {
@@ -332,11 +333,20 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
 
     // workgroup -> (batch, key/value head, key tile); the key tiles with the
     // most visible queries (the first ones, for causal problems) come first
-    const int kvh = p.B * p.Hkv;
-    int kt, kvflat, unused;
-    bwd_order(blockIdx.x, kvh, 1, p.n_ktiles, p.group_dkv, kvflat, unused, kt);
-    const int b = kvflat / p.Hkv;
-    const int hkv = kvflat - b * p.Hkv;
+    int b, hkv, kt;
+    if (VARLEN && p.compact_dkv) {
+        // compact grid: slot k of key/value head hkv, key tiles from 0 up (varlen_slot)
+        const int k = blockIdx.x / p.Hkv;
+        hkv = blockIdx.x - k * p.Hkv;
+        if (!varlen_slot<false>(p.cu_k, p.total_k, p.B, p.n_ktiles, C::ROWS, k, b, kt)) return;
+        b = __builtin_amdgcn_readfirstlane(b);
+        kt = __builtin_amdgcn_readfirstlane(kt);
+    } else {
+        int kvflat, unused;
+        bwd_order(blockIdx.x, p.B * p.Hkv, 1, p.n_ktiles, p.group_dkv, kvflat, unused, kt);
+        b = kvflat / p.Hkv;
+        hkv = kvflat - b * p.Hkv;
+    }
     const int k0 = kt * C::ROWS;
     const int wk0 = k0 + 32 * w;
     const int key = wk0 + n;
@@ -507,13 +517,24 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams pin) {
 
     // workgroup -> (batch, query head, query tile): heads first, and for
     // causal problems the query tiles with the most keys first
-    const int kvh = p.B * p.Hkv;
-    int t_ord, kvflat, gi;
-    bwd_order(blockIdx.x, kvh, p.group, p.n_qtiles, p.group_dq, kvflat, gi, t_ord);
-    const int b = kvflat / p.Hkv;
-    const int hkv = kvflat - b * p.Hkv;
-    const int hq = hkv * p.group + gi;
-    const int qt = CAUSAL ? p.n_qtiles - 1 - t_ord : t_ord;
+    int b, hkv, hq, qt;
+    if (VARLEN && p.compact_dq) {
+        // compact grid: slot k of query head x, query tiles from the last down (varlen_slot)
+        const int k = blockIdx.x / p.Hq;
+        const int x = blockIdx.x - k * p.Hq;
+        hkv = x % p.Hkv;
+        hq = hkv * p.group + x / p.Hkv;
+        if (!varlen_slot<true>(p.cu_q, p.total_q, p.B, p.n_qtiles, C::ROWS, k, b, qt)) return;
+        b = __builtin_amdgcn_readfirstlane(b);
+        qt = __builtin_amdgcn_readfirstlane(qt);
+    } else {
+        int t_ord, kvflat, gi;
+        bwd_order(blockIdx.x, p.B * p.Hkv, p.group, p.n_qtiles, p.group_dq, kvflat, gi, t_ord);
+        b = kvflat / p.Hkv;
+        hkv = kvflat - b * p.Hkv;
+        hq = hkv * p.group + gi;
+        qt = CAUSAL ? p.n_qtiles - 1 - t_ord : t_ord;
+    }
     const int q0 = qt * C::ROWS;
     const int wq0 = q0 + 32 * w;
     const int qrow = wq0 + n;
@@ -634,9 +655,13 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     // grids: Nk / Nq are the (largest) lengths; packed workgroups past their
-    // sequence's end return at once
+    // sequence's end return at once.  A packed batch whose padded grid would
+    // be 8 times the tiles that exist takes the compact grid instead
+    // (varlen_compact in fa_varlen.hpp).
     pp.n_ktiles = (p.Nk + C::ROWS - 1) / C::ROWS;
-    const int64_t kv_grid = (int64_t)pp.n_ktiles * p.B * p.Hkv;
+    pp.compact_dkv = VARLEN && varlen_compact(p.total_k, p.B, pp.n_ktiles, C::ROWS) ? 1 : 0;
+    const int64_t kv_grid = pp.compact_dkv ? varlen_slots(p.total_k, p.B, pp.n_ktiles, C::ROWS) * p.Hkv
+                                           : (int64_t)pp.n_ktiles * p.B * p.Hkv;
     if (kv_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if (kv_grid > 0) {
         if constexpr (FA_BWD_SPLIT_DKV && D == 128) {
@@ -652,7 +677,9 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     pp.n_qtiles = (p.Nq + C::ROWS - 1) / C::ROWS;
-    const int64_t q_grid = (int64_t)pp.n_qtiles * p.B * p.Hq;
+    pp.compact_dq = VARLEN && varlen_compact(p.total_q, p.B, pp.n_qtiles, C::ROWS) ? 1 : 0;
+    const int64_t q_grid = pp.compact_dq ? varlen_slots(p.total_q, p.B, pp.n_qtiles, C::ROWS) * p.Hq
+                                         : (int64_t)pp.n_qtiles * p.B * p.Hq;
     if (q_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if (q_grid > 0)
         e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, VARLEN>),

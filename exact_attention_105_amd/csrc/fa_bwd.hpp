@@ -33,6 +33,8 @@ struct BwdParams {
     const int* cu_k;
     int total_q;
     int total_k;
+    int compact_dkv;     // set by the launcher: 1 = the compact grid of varlen_slot for the
+    int compact_dq;      // dK/dV (key tiles) or dQ (query tiles) kernel, 0 = the padded grid
 };
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);

@@ -165,7 +165,18 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
     // for a variable-length batch, b is the sequence.
     FwdParams p = pin;
     int b, hq, hkv, qt;
-    tile_of<CAUSAL>(p, blockIdx.x, b, hq, hkv, qt);
+    if (VARLEN && vp.compact) {
+        // compact grid: slot k of query head x (heads innermost), see varlen_slot
+        const int k = blockIdx.x / p.Hq;
+        const int x = blockIdx.x - k * p.Hq;
+        hkv = x % p.Hkv;
+        hq = hkv * p.group + x / p.Hkv;
+        if (!varlen_slot<true>(vp.cu_q, vp.total_q, p.B, p.n_qtiles, C::BM, k, b, qt)) return;
+        b = __builtin_amdgcn_readfirstlane(b);
+        qt = __builtin_amdgcn_readfirstlane(qt);
+    } else {
+        tile_of<CAUSAL>(p, blockIdx.x, b, hq, hkv, qt);
+    }
     const int q0 = qt * C::BM;
     const int wq0 = q0 + w * C::RW;              // first row of this wave
 
@@ -496,7 +507,9 @@ static hipError_t launch_one(const FwdParams& p, const VarlenParams& vp, hipStre
     pp.n_qtiles = (p.Nq + C::BM - 1) / C::BM;
     const long long kv_rows = VARLEN ? (long long)vp.total_k : (long long)p.B * p.Nk;
     pp.kv_group = stream_group(kv_rows * p.Hkv * D * 2 * 2);
-    const long long grid = (long long)pp.n_qtiles * pp.n_heads;
+    vv.compact = VARLEN && varlen_compact(vp.total_q, p.B, pp.n_qtiles, C::BM) ? 1 : 0;
+    const long long grid = vv.compact ? varlen_slots(vp.total_q, p.B, pp.n_qtiles, C::BM) * p.Hq
+                                      : (long long)pp.n_qtiles * pp.n_heads;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     void* args[] = {&pp, &vv};

@@ -43,13 +43,19 @@ _NP = {"bf16": np.uint16, "e4m3": np.uint8, "f64": np.float64}
 _default = None
 
 
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
 def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH, rot_src: str = _ROT_SRC,
-          bwd_src: str = _BWD_SRC) -> str:
-    """Compile the oracle C sources into a shared library with gcc (IEEE semantics)."""
+          bwd_src: str = _BWD_SRC, sanitize: bool = False) -> str:
+    """Compile the oracle C sources into a shared library with gcc (IEEE semantics);
+    ``sanitize`` adds AddressSanitizer and UndefinedBehaviorSanitizer (a test
+    build: load it in a process that preloads libasan)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-fno-fast-math", "-ffp-contract=off", src, rot_src, bwd_src, "-o", tmp, "-lm"]
+               "-fno-fast-math", "-ffp-contract=off", *(SANITIZE_FLAGS if sanitize else []),
+               src, rot_src, bwd_src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out

@@ -216,7 +216,17 @@ def make_grad_output(B, Hq, Nq, d, seed):
 VARLEN_WORKLOADS = {
     # 24 causal sequences, lengths log-uniform in [128, 8192] (seed 105020), 16 heads, d 128
     "varlen_mix": dict(n_seqs=24, lo=128, hi=8192, Hq=16, Hkv=16, d=128, causal=True, seed=105020),
+    # one 8192-token sequence packed with 255 sequences of 128 tokens, causal, 16 heads, d 128
+    "varlen_skew": dict(n_seqs=256, long=8192, short=128, Hq=16, Hkv=16, d=128, causal=True, seed=105021),
 }
+
+
+def workload_lengths(w):
+    """Sequence lengths of a VARLEN_WORKLOADS entry: log-uniform (lo, hi) or
+    one long sequence followed by n_seqs - 1 short ones."""
+    if "long" in w:
+        return np.array([w["long"]] + [w["short"]] * (w["n_seqs"] - 1), dtype=np.int64)
+    return varlen_lengths(w["n_seqs"], w["lo"], w["hi"], w["seed"])
 
 
 def varlen_lengths(n_seqs, lo, hi, seed):

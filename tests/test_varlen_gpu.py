@@ -10,7 +10,7 @@ import torch
 import oracle
 from exact_attention_105_amd import fwd, fwd_varlen
 from gpu_util import compare_bf16, say
-from synth.inputs import VARLEN_WORKLOADS, make_varlen_inputs, varlen_lengths
+from synth.inputs import VARLEN_WORKLOADS, make_varlen_inputs, workload_lengths
 
 pytestmark = pytest.mark.gpu
 
@@ -48,11 +48,19 @@ CASES = [
     ([77, 256, 5], [200, 100, 5], 2, 2, 64, True),
     ([500, 3, 260], [1, 700, 0], 4, 2, 128, False),       # a single key, an empty key side
     ([1000], None, 8, 2, 128, True),
+    # more sequences than a wave has lanes (the grid's slot search spans several 64-sequence chunks),
+    # lengths from 0 to 400 with empty and one-row sequences among them
+    (np.random.default_rng(150).integers(0, 401, 150).tolist(), None, 2, 1, 64, True),
+    (np.random.default_rng(70).integers(0, 300, 70).tolist(), None, 2, 2, 128, False),
+    # padded grids 8x or more the tiles that exist: these take the compact grid (one slot per tile,
+    # found by a search over the sequences' tile counts), with 2 and 5 chunks of 64 sequences
+    ([2000] + [10] * 100, None, 2, 1, 128, True),
+    ([3000] + np.random.default_rng(300).integers(0, 21, 299).tolist(), None, 2, 2, 64, False),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}H{c[2]}/{c[3]}d{c[4]}{'c' if c[5] else ''}"
-                                             for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[(f"{c[0]}" if len(c[0]) <= 8 else f"{len(c[0])}seqs")
+                                             + f"x{c[1]}H{c[2]}/{c[3]}d{c[4]}{'c' if c[5] else ''}" for c in CASES])
 def test_varlen_matches_oracle(case):
     lq, lk, Hq, Hkv, d, causal = case
     lk = lq if lk is None else lk
@@ -81,14 +89,16 @@ def test_equal_lengths_match_the_batch_kernel_bit_for_bit():
         assert np.array_equal(o, ob) and np.array_equal(lse, lb)
 
 
-def test_varlen_mix_workload_sampled_rows():
-    """The ragged bench workload at full size: sampled rows of every sequence
-    against the oracle on that sequence."""
-    w = VARLEN_WORKLOADS["varlen_mix"]
-    lens = varlen_lengths(w["n_seqs"], w["lo"], w["hi"], w["seed"])
+@pytest.mark.parametrize("name", ["varlen_mix", "varlen_skew"])
+def test_varlen_workload_sampled_rows(name):
+    """The ragged bench workloads at full size (varlen_skew takes the compact
+    grid): sampled rows of every sequence against the oracle on that
+    sequence."""
+    w = VARLEN_WORKLOADS[name]
+    lens = workload_lengths(w)
     x = make_varlen_inputs(lens, lens, w["Hq"], w["Hkv"], w["d"], w["seed"])
     scale = 1.0 / math.sqrt(w["d"])
-    say(f"varlen_mix: {len(lens)} sequences, {int(lens.sum())} tokens")
+    say(f"{name}: {len(lens)} sequences, {int(lens.sum())} tokens")
     o, lse = run_varlen(x, w["causal"], scale)
     rng = np.random.default_rng(3)
     cu = x["cu_q"]
@@ -100,7 +110,7 @@ def test_varlen_mix_workload_sampled_rows():
         rows = rng.choice(w["Hq"] * L, size=min(16, w["Hq"] * L), replace=False)   # flat (h, i) within the sequence
         o_ref, lse_ref = oracle.attention(qs, ks, vs, causal=w["causal"], scale=scale, rows=rows)
         h, i = rows // L, rows % L
-        compare_bf16(o[cu[s] + i, h], lse[h, cu[s] + i], o_ref, lse_ref, f"varlen_mix sequence {s} (len {L})")
+        compare_bf16(o[cu[s] + i, h], lse[h, cu[s] + i], o_ref, lse_ref, f"{name} sequence {s} (len {L})")
 
 
 def run_varlen_bwd(x, do_bits, causal, scale):
@@ -125,10 +135,14 @@ BWD_CASES = [
     ([77, 256, 5], [200, 100, 5], 2, 1, 64, True),
     ([500, 3, 260], [1, 700, 0], 4, 2, 128, False),
     ([300, 300], [300, 300], 8, 2, 128, True),
+    # the compact grids of the dK/dV and dQ kernels (padded grids 8x or more the tiles that exist)
+    ([2000] + [10] * 100, None, 2, 1, 128, True),
+    ([1500] + np.random.default_rng(151).integers(0, 21, 150).tolist(), None, 2, 2, 64, False),
 ]
 
 
-@pytest.mark.parametrize("case", BWD_CASES, ids=[f"{c[0]}x{c[1]}H{c[2]}/{c[3]}d{c[4]}{'c' if c[5] else ''}"
+@pytest.mark.parametrize("case", BWD_CASES, ids=[(f"{c[0]}" if len(c[0]) <= 8 else f"{len(c[0])}seqs")
+                                                 + f"x{c[1]}H{c[2]}/{c[3]}d{c[4]}{'c' if c[5] else ''}"
                                                  for c in BWD_CASES])
 def test_varlen_backward_matches_oracle(case):
     from test_bwd_gpu import compare
