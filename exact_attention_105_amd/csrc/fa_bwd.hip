@@ -123,49 +123,13 @@ __device__ __forceinline__ void copy_pair(const char* a, const char* b, int r0, 
     const int c_row = lane / C::UPR, c_su = lane % C::UPR;
     const char* abase = a + (int64_t)r0 * stride;
     const char* bbase = b + (int64_t)r0 * stride;
-    const int last = N - 1 - r0;
 #pragma unroll
     for (int t = 0; t < PW; ++t) {
         const int piece = w * PW + t;
         const int row = piece * C::RPC + c_row;
-        const uint32_t off = min(row, last) * (uint32_t)stride + ((c_su ^ C::swz(row)) << 4);
+        const uint32_t off = copy_src_row(row, r0, N) * (uint32_t)stride + ((c_su ^ C::swz(row)) << 4);
         dma16(abase, off, dst + piece * 1024);
         dma16(bbase, off, dst + BYTES + piece * 1024);
-    }
-}
-
-// Workgroup -> (key/value head kvflat = b*Hkv + hkv, member gi of its
-// `width` heads, tile rank t) over kvh*width units of n_tiles tiles.  The
-// hardware hands workgroups to the 8 XCDs round-robin (id mod 8).
-//  * group == 0: ranks outermost, units inner (all heads together, the
-//    heaviest causal tiles first).
-//  * group > 0 and kvh a multiple of 8: XCD x owns the key/value heads
-//    congruent to x mod 8 and takes them `group` at a time, ranks outermost
-//    within each group, so the workgroups resident on an XCD share the rows
-//    they stream through its L2 (stream_group picks this once those rows
-//    outgrow the memory-side cache).
-__device__ __forceinline__ void bwd_order(int bid, int kvh, int width, int n_tiles, int group,
-                                          int& kvflat, int& gi, int& t) {
-    if (group > 0 && (kvh & 7) == 0) {
-        const int xcd = bid & 7;
-        const int L = bid >> 3;
-        const int nkv = kvh >> 3;                        // key/value heads on this XCD
-        const int G = min(group, nkv);
-        const int per = G * width * n_tiles;             // workgroups of one full group
-        const int gidx = L / per;
-        const int r = L - gidx * per;
-        const int ge = min(G, nkv - gidx * G) * width;   // units in this group
-        t = r / ge;
-        const int hl = gidx * G * width + (r - t * ge);
-        const int kg = hl / width;
-        gi = hl - kg * width;
-        kvflat = xcd + 8 * kg;
-    } else {
-        const int n = kvh * width;
-        t = bid / n;
-        const int x = bid - t * n;
-        kvflat = x % kvh;
-        gi = x / kvh;
     }
 }
 
@@ -554,12 +518,9 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams pin) {
     const char* Kh = reinterpret_cast<const char*>(p.k) + kvbase;
     const char* Vh = reinterpret_cast<const char*>(p.v) + kvbase;
 
-    int kend = p.Nk;
-    if (CAUSAL) kend = min(kend, max(q0 + C::ROWS + p.causal_shift, 0));
+    const int kend = key_end(q0, C::ROWS, p.Nk, p.causal_shift, CAUSAL);
     const int n_tiles = __builtin_amdgcn_readfirstlane((kend + C::T - 1) / C::T);
-    int wkend = p.Nk;
-    if (CAUSAL) wkend = min(wkend, max(wq0 + 32 + p.causal_shift, 0));
-    wkend = __builtin_amdgcn_readfirstlane(wkend);
+    const int wkend = __builtin_amdgcn_readfirstlane(key_end(wq0, 32, p.Nk, p.causal_shift, CAUSAL));
 
     bf16x8 qf[C::KS], df[C::KS];
     load_b_rows<D>(reinterpret_cast<const char*>(p.q) + qbase, qrow, p.Nq, g, qf, QSTR);

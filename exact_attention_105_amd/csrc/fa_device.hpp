@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_index.hpp"
+
 namespace fa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -28,23 +30,6 @@ typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-struct FwdParams {
-    const void* q;
-    const void* k;
-    const void* v;
-    void* o;
-    float* lse;
-    int B, Hq, Hkv, Nq, Nk;
-    int group;          // Hq / Hkv
-    int n_qtiles;       // ceil(Nq / rows per workgroup)
-    int n_heads;        // B * Hq
-    int causal_shift;   // Nk - Nq: key j visible to query i iff j <= i + causal_shift
-    float c;            // |scale| (* sq * sk for fp8) * log2(e): exponent of 2 per raw score
-    float o_scale;      // multiplies the normalised output (sv for fp8, 1 for bf16)
-    uint32_t q_sign;    // XOR mask applied to Q bit patterns (flips the sign when scale < 0)
-    int kv_group;       // causal order: 0 walks all heads together; G > 0 takes each XCD's
-                        // key/value heads G at a time (stream_group)
-};
 
 __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -108,86 +93,6 @@ __device__ __forceinline__ u32x4 lds_load16(const char* base, uint32_t off) {
     return *reinterpret_cast<const u32x4*>(base + off);
 }
 
-// Heads are enumerated so that the Hq/Hkv query heads sharing one key/value
-// head get flat indices that are congruent modulo 8 whenever B*Hkv is a
-// multiple of 8; the hardware hands workgroups to the 8 XCDs round-robin, so
-// those heads (and their K/V traffic) land on the same XCD and its L2.
-__device__ __forceinline__ void head_of(const FwdParams& p, int x, int& b, int& hq, int& hkv) {
-    const int kvflat = x % (p.B * p.Hkv);
-    const int gi = x / (p.B * p.Hkv);
-    b = kvflat / p.Hkv;
-    hkv = kvflat % p.Hkv;
-    hq = hkv * p.group + gi;
-}
-
-// Workgroup -> (batch, query head, key/value head, query tile) for the
-// prefill kernels.  The hardware hands workgroups to the 8 XCDs round-robin
-// (id mod 8).
-//  * Causal problems: consecutive ids walk the heads first (head_of), the
-//    query tiles heaviest first, so every head's long rows start at the
-//    beginning of the launch (longest-first scheduling; the tail is made of
-//    the shortest tiles).
-//  * Non-causal problems, when B*Hkv is a multiple of 8: XCD x owns the
-//    key/value heads congruent to x mod 8 and walks them one at a time --
-//    the query heads of a key/value head next to each other, each head's
-//    query tiles consecutively -- so the workgroups resident on an XCD stream
-//    the same keys and values through its L2 together.  (On a causal problem
-//    whose keys and values fit the memory-side cache, 16K tokens x 32 heads,
-//    this order cut the fetched bytes about 8x but lost more to the late
-//    start of the last heads' long rows than it gained.)
-//  * Causal problems whose keys and values outgrow the 256 MB memory-side
-//    cache (kv_group > 0): XCD x again owns the key/value heads congruent to
-//    x mod 8, but walks them kv_group at a time, heaviest query tiles first
-//    within each group.  The heads-first order streams every head's keys at
-//    once; past that cache its re-reads go to HBM, and measured launches ran
-//    up to 1.6x longer (2048 tokens x 1024 heads of d = 128).
-template <bool CAUSAL>
-__device__ __forceinline__ void tile_of(const FwdParams& p, int bid, int& b, int& hq, int& hkv, int& qt) {
-    const int kvh = p.B * p.Hkv;
-    int t_ord;
-    if (CAUSAL && p.kv_group > 0 && (kvh & 7) == 0) {
-        const int xcd = bid & 7;
-        const int L = bid >> 3;
-        const int nkv = kvh >> 3;                       // key/value heads on this XCD
-        const int G = min(p.kv_group, nkv);
-        const int per = G * p.group * p.n_qtiles;       // tiles of one full group
-        const int gidx = L / per;
-        const int r = L - gidx * per;
-        const int ge = min(G, nkv - gidx * G) * p.group; // query heads in this group
-        t_ord = r / ge;
-        const int hl = gidx * G * p.group + (r - t_ord * ge);
-        const int kg = hl / p.group;
-        const int gi = hl - kg * p.group;
-        const int kvflat = xcd + 8 * kg;
-        b = kvflat / p.Hkv;
-        hkv = kvflat - b * p.Hkv;
-        hq = hkv * p.group + gi;
-        qt = p.n_qtiles - 1 - t_ord;
-        return;
-    }
-    if (!CAUSAL && (kvh & 7) == 0) {
-        const int xcd = bid & 7;
-        const int L = bid >> 3;
-        const int hl = L / p.n_qtiles;          // head index within this XCD's share
-        t_ord = L - hl * p.n_qtiles;
-        const int kg = hl / p.group;
-        const int gi = hl - kg * p.group;
-        const int kvflat = xcd + 8 * kg;
-        b = kvflat / p.Hkv;
-        hkv = kvflat - b * p.Hkv;
-        hq = hkv * p.group + gi;
-    } else {
-        t_ord = bid / p.n_heads;
-        head_of(p, bid - t_ord * p.n_heads, b, hq, hkv);
-    }
-    qt = CAUSAL ? (p.n_qtiles - 1 - t_ord) : t_ord;
-}
-
-// Group size for the XCD-local orders of launches whose workgroups all
-// stream one set of per-head tensors (keys and values for the forward and
-// dQ kernels, queries and output gradients for dK/dV) holding `bytes` bytes
-// in all: 2 above the 256 MiB memory-side cache, else 0 (heads first).
-inline int stream_group(long long bytes) { return bytes > (256LL << 20) ? 2 : 0; }
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;

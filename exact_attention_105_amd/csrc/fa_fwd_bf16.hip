@@ -211,13 +211,10 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
     // (The bounds are workgroup- or wave-uniform; readfirstlane keeps them,
     // and the loop control built on them, in scalar registers -- the integer
     // division behind the head mapping is computed on the vector ALU.)
-    int kend = p.Nk;
-    if (CAUSAL) kend = min(kend, max(q0 + C::BM + p.causal_shift, 0));
+    const int kend = key_end(q0, C::BM, p.Nk, p.causal_shift, CAUSAL);
     const int n_tiles = __builtin_amdgcn_readfirstlane((kend + C::BN - 1) / C::BN);
     // Keys this wave needs (its other tiles only take part in the copies).
-    int wkend = p.Nk;
-    if (CAUSAL) wkend = min(wkend, max(wq0 + C::RW + p.causal_shift, 0));
-    wkend = __builtin_amdgcn_readfirstlane(wkend);
+    const int wkend = __builtin_amdgcn_readfirstlane(key_end(wq0, C::RW, p.Nk, p.causal_shift, CAUSAL));
 
     // Q rows of this lane as MFMA B operands, resident for the whole loop.
     bf16x8 qf[C::NQB][C::KS];
@@ -283,11 +280,10 @@ __global__ __launch_bounds__(256, Bf16Cfg<D>::OCC) void fa_fwd_bf16_kernel(FwdPa
                 dma16(vb, dv_off[t], vdst + t * 1024);
             }
         } else {
-            const int last = p.Nk - 1 - key0;
 #pragma unroll
             for (int t = 0; t < C::CPW; ++t) {
                 const int row = (w * C::CPW + t) * C::RPC + c_row;
-                const int rc = min(row, last);
+                const int rc = copy_src_row(row, key0, p.Nk);
                 dma16(kb, rc * (uint32_t)KVSTR + ((c_su ^ C::kswz(row)) << 4), kdst + t * 1024);
                 dma16(vb, rc * (uint32_t)KVSTR + ((c_su ^ C::vswz(row)) << 4), vdst + t * 1024);
             }

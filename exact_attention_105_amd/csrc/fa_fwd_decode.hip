@@ -140,11 +140,10 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_decode_kernel(FwdParams p, int 
                 dma16(vb, dv_off[c], vdst + c * 1024);
             }
         } else {
-            const int last = p.Nk - 1 - key0;
 #pragma unroll
             for (int c = 0; c < kCH; ++c) {
                 const int row = 4 * c + c_row;
-                const int rc = min(row, last);
+                const int rc = copy_src_row(row, key0, p.Nk);
                 dma16(kb, rc * kROW + ((c_su ^ (row & 15)) << 4), kdst + c * 1024);
                 dma16(vb, rc * kROW + ((c_su ^ (4 * (row & 3))) << 4), vdst + c * 1024);
             }

@@ -100,12 +100,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
 
     // (readfirstlane keeps these uniform bounds, and the loop control built
     // on them, in scalar registers)
-    int kend = p.Nk;
-    if (CAUSAL) kend = min(kend, max(q0 + C::BM + p.causal_shift, 0));
+    const int kend = key_end(q0, C::BM, p.Nk, p.causal_shift, CAUSAL);
     const int n_tiles = __builtin_amdgcn_readfirstlane((kend + C::BN - 1) / C::BN);
-    int wkend = p.Nk;
-    if (CAUSAL) wkend = min(wkend, max(wq0 + 32 + p.causal_shift, 0));
-    wkend = __builtin_amdgcn_readfirstlane(wkend);
+    const int wkend = __builtin_amdgcn_readfirstlane(key_end(wq0, 32, p.Nk, p.causal_shift, CAUSAL));
 
     // Q as B operands: k-step ks covers d = 64*ks + 32*g + [0, 32).
     i32x8 qf[2];
@@ -167,11 +164,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
                 dma16(vb, dv_off[t], vdst + t * 1024);
             }
         } else {
-            const int last = p.Nk - 1 - key0;
 #pragma unroll
             for (int t = 0; t < C::CPW; ++t) {
                 const int row = (w * C::CPW + t) * C::RPC + c_row;
-                const int rc = min(row, last);
+                const int rc = copy_src_row(row, key0, p.Nk);
                 dma16(kb, rc * C::ROW + ((c_su ^ k8_swz(row)) << 4), kdst + t * 1024);
                 dma16(vb, rc * C::ROW + ((c_su ^ v8_swz(row)) << 4), vdst + t * 1024);
             }
