@@ -132,14 +132,14 @@ def _code_only(text: bytes) -> bytes:
 
 def kernel_source_hash(cfg) -> str:
     """Hash of what the workload's kernel is compiled from: its source file,
-    the shared device header (and, for the bf16 prefill kernel, the
+    the shared device and index headers (and, for the bf16 prefill kernel, the
     variable-length header it includes), code only, comments ignored, and
     that file's extra compiler flags."""
     from exact_attention_105_amd import build as _build
     src = kernel_source(cfg)
     csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
     h = hashlib.sha256()
-    for f in (src, "fa_device.hpp") + (("fa_varlen.hpp",) if src == "fa_fwd_bf16.hip" else ()):
+    for f in (src, "fa_device.hpp", "fa_index.hpp") + (("fa_varlen.hpp",) if src == "fa_fwd_bf16.hip" else ()):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + _code_only(fh.read()))
     h.update(" ".join(_build.HIPCC_FLAGS + _build.SOURCE_FLAGS.get(src, [])).encode())
@@ -266,7 +266,7 @@ def gemm_reference(args):
     del c
 
 
-ROTATE_SOURCES = ("fa_rotate.hip", "fa_device.hpp", "fa_launch.hpp")
+ROTATE_SOURCES = ("fa_rotate.hip", "fa_device.hpp", "fa_index.hpp", "fa_launch.hpp")
 
 
 def rotate_source_hash() -> str:
@@ -617,7 +617,7 @@ def bwd_source_hash() -> str:
     from exact_attention_105_amd import build as _build
     csrc = os.path.join(ROOT, "exact_attention_105_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("fa_bwd.hip", "fa_bwd.hpp", "fa_device.hpp"):
+    for f in ("fa_bwd.hip", "fa_bwd.hpp", "fa_device.hpp", "fa_index.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + _code_only(fh.read()))
     h.update(" ".join(_build.HIPCC_FLAGS + _build.SOURCE_FLAGS.get("fa_bwd.hip", [])).encode())
