@@ -3,6 +3,7 @@
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <mutex>
 
@@ -18,6 +19,26 @@ constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
 }  // namespace
+
+namespace fa {
+
+size_t test_extra_lds(size_t static_lds) {
+    static const size_t want = [] {
+        const char* v = getenv("FA_TEST_EXTRA_LDS");
+        const long long x = v == nullptr ? 0 : atoll(v);
+        return (size_t)(x < 0 ? 0 : x);
+    }();
+    constexpr size_t kLdsPerCu = 160 << 10;      // gfx950
+    // total per workgroup while the hook is on: no more than the decode
+    // kernel's own static LDS, well inside the 160 KiB limit
+    constexpr size_t kCap = 128 << 10;
+    // a kernel whose own LDS already limits it to one workgroup per CU is left alone
+    if (want == 0 || 2 * static_lds > kLdsPerCu || static_lds >= kCap) return 0;
+    const size_t room = kCap - static_lds;
+    return want < room ? want : room;
+}
+
+}  // namespace fa
 
 // Split-KV partials for fa_fwd_splitkv_noalloc: one copy per GPU, held until
 // the process ends.  In host code `scratch` names a host-side stand-in, not

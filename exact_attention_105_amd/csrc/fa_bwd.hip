@@ -39,6 +39,7 @@
 
 #include "fa_bwd.hpp"
 #include "fa_device.hpp"
+#include "fa_launch.hpp"
 #include "fa_varlen.hpp"
 
 
@@ -626,14 +627,14 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     if (kv_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if (kv_grid > 0) {
         if constexpr (FA_BWD_SPLIT_DKV && D == 128) {
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDV, VARLEN>),
-                                dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
+            const void* kdv = reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDV, VARLEN>);
+            e = hipLaunchKernel(kdv, dim3((unsigned)kv_grid), dim3(256), args, test_extra_lds(KvCfg<D, CAUSAL, kOnlyDV>::LDS), stream);
             if (e != hipSuccess) return e;
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDK, VARLEN>),
-                                dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
+            const void* kdk = reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDK, VARLEN>);
+            e = hipLaunchKernel(kdk, dim3((unsigned)kv_grid), dim3(256), args, test_extra_lds(KvCfg<D, CAUSAL, kOnlyDK>::LDS), stream);
         } else {
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kBoth, VARLEN>),
-                                dim3((unsigned)kv_grid), dim3(256), args, 0, stream);
+            const void* kboth = reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kBoth, VARLEN>);
+            e = hipLaunchKernel(kboth, dim3((unsigned)kv_grid), dim3(256), args, test_extra_lds(KvCfg<D, CAUSAL, kBoth>::LDS), stream);
         }
         if (e != hipSuccess) return e;
     }
@@ -642,9 +643,10 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     const int64_t q_grid = pp.compact_dq ? varlen_slots(p.total_q, p.B, pp.n_qtiles, C::ROWS) * p.Hq
                                          : (int64_t)pp.n_qtiles * p.B * p.Hq;
     if (q_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    if (q_grid > 0)
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, VARLEN>),
-                            dim3((unsigned)q_grid), dim3(256), args, 0, stream);
+    if (q_grid > 0) {
+        const void* kdq = reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, VARLEN>);
+        e = hipLaunchKernel(kdq, dim3((unsigned)q_grid), dim3(256), args, test_extra_lds(C::LDS), stream);
+    }
     return e;
 }
 

@@ -509,8 +509,8 @@ static hipError_t launch_one(const FwdParams& p, const VarlenParams& vp, hipStre
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     void* args[] = {&pp, &vv};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_bf16_kernel<D, CAUSAL, VARLEN>),
-                           dim3((unsigned)grid), dim3(256), args, 0, stream);
+    const void* kernel = reinterpret_cast<const void*>(&fa_fwd_bf16_kernel<D, CAUSAL, VARLEN>);
+    return hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(256), args, test_extra_lds(C::LDS), stream);
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream) {

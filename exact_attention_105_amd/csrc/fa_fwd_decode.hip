@@ -348,8 +348,8 @@ hipError_t launch_fwd_decode_split(const FwdParams& p, bool causal, int n_splits
     int ns = n_splits;
     float* w = ws;
     void* args[] = {&pp, &c, &ns, &w};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_decode_kernel), dim3((unsigned)grid),
-                                   dim3(256), args, 0, stream);
+    const void* kernel = reinterpret_cast<const void*>(&fa_fwd_decode_kernel);
+    hipError_t e = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(256), args, test_extra_lds(kLDS), stream);
     if (e != hipSuccess || n_splits == 1) return e;
     const long long rows = (long long)p.B * p.Hq * p.Nq;
     if (rows > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;

@@ -322,8 +322,8 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     void* args[] = {&pp};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fa_fwd_fp8_kernel<CAUSAL>),
-                           dim3((unsigned)grid), dim3(256), args, 0, stream);
+    const void* kernel = reinterpret_cast<const void*>(&fa_fwd_fp8_kernel<CAUSAL>);
+    return hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(256), args, test_extra_lds(Fp8Cfg::LDS), stream);
 }
 
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream) {

@@ -7,6 +7,17 @@
 
 namespace fa {
 
+// Dynamic LDS, in bytes, to launch a kernel that declares `static_lds` bytes
+// of LDS with, never touched by it: the value of the environment variable
+// FA_TEST_EXTRA_LDS (decimal, read once per process; 0 when unset), cut so
+// that static plus dynamic LDS stays within 128 KiB (the decode kernel's own
+// static LDS; gfx950 allows 160 KiB per workgroup), and 0 for a kernel whose
+// static LDS already keeps it to one workgroup per CU (the decode kernel).
+// A test hook: it lowers the number of workgroups resident on each CU, so
+// tests can check that results do not depend on occupancy.  Used by the
+// prefill, decode and backward launches.
+size_t test_extra_lds(size_t static_lds);
+
 // bf16 inputs, head dim 64 or 128.  Fills n_qtiles itself.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 
