@@ -26,6 +26,8 @@
 // rows one ds_read_b128 touches hit distinct banks; V by
 // 2*((row/2 mod 2) + 2*(row/8 mod 2)), which separates the 8 rows one
 // transposing read touches.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
@@ -183,15 +185,20 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
 
     if (n_tiles > 0) issue_tile(0, 0);
 
-    for (int j = 0; j < n_tiles; ++j) {
-        const int stage = j & 1;
+    // One key tile.  Templated on the LDS stage so that every LDS address is a
+    // loop-invariant per-lane register plus an immediate (+1.7 % over a
+    // runtime stage, bit-identical); the barrier carries no memory fence, the
+    // copies being awaited with vmcnt.
+    const float inv_c = 1.0f / p.c;
+    auto tile = [&](auto stage_c, int j) {
+        constexpr int stage = decltype(stage_c)::value;
         FA_WAIT_VMCNT(0);
-        __syncthreads();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
         const int key0 = j * C::BN;
         if (key0 >= wkend) {
             if (j + 1 < n_tiles) issue_tile(j + 1, stage ^ 1);
-            continue;
+            return;
         }
         const lds_char* kb = smem + stage * C::STAGE;
         const lds_char* vb = kb + C::TILE;
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
             const float mnew = move ? mx : mref;
             const float alpha = fast_exp2(mref - mnew);   // 0 at the first move, 1 if unmoved
             mref = mnew;
-            thr = (mnew + kP8Slack) / p.c;
+            thr = (mnew + kP8Slack) * inv_c;
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
@@ -274,6 +281,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_fp8_kernel(FwdParams p) {
         order_reads_ahead<C::DB, 4, FA_FP8_PF_V>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
+    };
+    for (int j = 0; j < n_tiles; j += 2) {
+        tile(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, j + 1);
     }
 
     // Epilogue: normalise, stage O as bf16 in LDS, coalesced 16-byte stores.
