@@ -16,6 +16,9 @@ K is zero except key 0, Q[h, r, :] = a/64 with a = ((h Nq + r) >> 18) mod 8,
 scale 1, so key 0 scores 2a and every row has the closed form
   O = (e^{2a} V[0] + sum_{k >= 1} V[k]) / (e^{2a} + 63),  LSE = ln(e^{2a} + 63).
 Every row of O and LSE is compared on the GPU (NaN-poisoned beforehand).
+
+Backward: fa_bwd over the same 2^24 - 1 keys, its dV row of the spike against
+its closed form and every gradient finite (outputs NaN-poisoned).
 """
 import math
 
@@ -160,3 +163,41 @@ def test_query_side_at_max():
         worst = max(worst, float((blk - tab_o[ai[r0:r0 + (1 << 20)]][:, None]).abs().max()))
     say(f"  query side: max|dO| = {worst:.3e}, max|dLSE| = {lerr:.3e} over {o2.shape[0]} rows")
     assert worst <= BF16_MAX_ABS and lerr <= LSE_MAX_ABS
+
+
+def test_backward_key_side_at_max(key_side):
+    """fa_bwd over the 2^24 - 1 keys (Nq = 64, causal): with dO = 1/64 in every
+    element, dV[s] = P_s * sum_i dO[i] = P_s per column (P_s = e^30 / Z, Z as
+    above), every other dV row is 64 P_0 / 64 = 1 / Z (about 1e-13), and dQ and
+    dK are of the order 1 - P_s (about 1e-6): all within the bf16 bounds of zero."""
+    from exact_attention_105_amd import bwd
+    k, v = key_side
+    dev = k.device
+    s = NK_MAX - 100
+    k[0, 0, s, :] = 1.0
+    try:
+        nq = 64
+        q = torch.full((1, 1, nq, 128), SPIKE_SCORE / 128.0, dtype=torch.bfloat16, device=dev)
+        say(f"max-size backward: Nq={nq} Nk={NK_MAX} causal")
+        o, l = fwd(q, k, v, causal=True, scale=1.0)
+        do = torch.full_like(q, 1.0 / 64.0)
+        dq = torch.full_like(q, float("nan"))
+        dk = torch.full_like(k, float("nan"))
+        dv = torch.full_like(v, float("nan"))
+        bwd(q, k, v, o, l, do, causal=True, scale=1.0, dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            assert bool(torch.isfinite(t).all()), f"{name} not finite (unwritten rows stay NaN)"
+        # rows see keys up to Nk - 64 + i: Z differs per row, P_s = e^30 / Z_i
+        ps = [math.exp(SPIKE_SCORE) / (math.exp(SPIKE_SCORE) + (NK_MAX - nq + i + 1) - 1) for i in range(nq)]
+        want_dvs = sum(ps) / 64.0
+        got = dv[0, 0, s].float()
+        err_s = float((got - want_dvs).abs().max())
+        others = float(dv[0, 0, torch.tensor([0, 1 << 23, NK_MAX - 200, NK_MAX - 1], device=dev)].float().abs().max())
+        dq_max = float(dq.float().abs().max())
+        dk_max = float(dk.float().abs().max())
+        say(f"  dV[spike] error {err_s:.3e} (value {want_dvs:.6f}); max |dV| elsewhere {others:.3e}; "
+            f"max |dQ| {dq_max:.3e}; max |dK| {dk_max:.3e}")
+        assert err_s <= BF16_MAX_ABS and others <= BF16_MAX_ABS and dq_max <= BF16_MAX_ABS and dk_max <= BF16_MAX_ABS
+    finally:
+        k[0, 0, s, :] = 0.0
