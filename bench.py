@@ -184,8 +184,13 @@ def cpu_model() -> str:
     return f"{name}{topo}, {len(os.sched_getaffinity(0))} logical CPUs available"
 
 
-def cpu_baseline(cfg, x, budget_s: float):
-    """Time the oracle on sampled rows of the workload for about budget_s seconds."""
+def cpu_baseline(cfg, x, budget_s: float, gpu_out=None):
+    """Time the oracle on sampled rows of the workload for about budget_s seconds.
+
+    With ``gpu_out`` = (O, LSE) of the timed launches (torch tensors), the
+    oracle rows of the timed batch are also compared with the GPU's rows:
+    max and mean |O - O_ref| and max |LSE - LSE_ref| for bf16, the relative
+    RMSE of O and max |LSE - LSE_ref| for fp8 (the bounds the tests apply)."""
     import oracle
     rng = np.random.default_rng(12345)
     total_rows = cfg.B * cfg.Hq * cfg.Nq
@@ -206,8 +211,8 @@ def cpu_baseline(cfg, x, budget_s: float):
     n = int(min(total_rows, max(n0, n0 * budget_s / max(dt0, 1e-6))))
     rows = np.sort(rng.choice(total_rows, size=n, replace=False))
     t0 = time.perf_counter()
-    oracle.attention(x["q"], x["k"], x["v"], causal=cfg.causal, scale=cfg.scale, dtype=cfg.dtype,
-                     descale=x.get("descale"), rows=rows)
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], causal=cfg.causal, scale=cfg.scale, dtype=cfg.dtype,
+                                      descale=x.get("descale"), rows=rows)
     dt = time.perf_counter() - t0
     i = rows % cfg.Nq
     vis = np.minimum(cfg.Nk, i + (cfg.Nk - cfg.Nq) + 1) if cfg.causal else np.full(rows.shape, cfg.Nk)
@@ -215,9 +220,24 @@ def cpu_baseline(cfg, x, budget_s: float):
     # the metric's FLOP convention: 4*d per visible (query, key) pair, with the
     # causal square problem counted at half the full-matrix work
     flops = 4.0 * cfg.d * float(vis.sum())
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
-            "sample": f"{n} uniformly sampled query rows of {cfg.name} ({n / total_rows:.2%} of the rows, "
-                      f"{flops / 1e9:.1f} GFLOP by the visible-key count) in {dt:.1f} s, fp64"}
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
+           "sample": f"{n} uniformly sampled query rows of {cfg.name} ({n / total_rows:.2%} of the rows, "
+                     f"{flops / 1e9:.1f} GFLOP by the visible-key count) in {dt:.1f} s, fp64"}
+    if gpu_out is not None:
+        import torch
+        o_gpu, lse_gpu = gpu_out
+        idx = torch.from_numpy(rows).to(o_gpu.device)
+        og = o_gpu.reshape(-1, cfg.d)[idx].float().cpu().double().numpy()
+        lg = lse_gpu.reshape(-1)[idx].double().cpu().numpy()
+        finite = np.isfinite(lse_ref)
+        lerr = float(np.abs(lg[finite] - lse_ref[finite]).max()) if finite.any() else 0.0
+        par = {"rows": int(n), "lse_max_abs": lerr}
+        if cfg.dtype == "bf16":
+            par.update(o_max_abs=float(np.abs(og - o_ref).max()), o_mean_abs=float(np.abs(og - o_ref).mean()))
+        else:
+            par["o_rrmse"] = float(np.linalg.norm(og - o_ref) / max(np.linalg.norm(o_ref), 1e-300))
+        res["parity"] = par
+    return res
 
 
 def copy_calibration(args):
@@ -807,7 +827,7 @@ def main():
         "wall_s_timed": wall,
     }
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget, gpu_out=(out, lse))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
