@@ -11,11 +11,13 @@
 // Three kernels on the caller's stream:
 //   1. fa_bwd_prep_kernel: D_i and the base-2 LSE per query row into the
 //      caller's workspace (a row that saw no key gets +inf, so its P is 0);
-//   2. fa_bwd_dkv_kernel: one workgroup owns 128 keys of one key/value head
-//      (32 per wave) and streams the Q and dO rows of every query head of
-//      its group through LDS in 32-row tiles; dK and dV accumulate in
-//      registers, so grouped-query sums need no atomics and the result is
-//      deterministic;
+//   2. dK and dV: a workgroup owns a block of keys of one key/value head and
+//      streams the Q and dO rows of every query head of its group through
+//      LDS; dK and dV accumulate in registers, so grouped-query sums need no
+//      atomics and the result is deterministic.  d = 64: fa_bwd_dkv_kernel,
+//      128 keys, one wave per 32 keys; d = 128: fa_bwd_dkv_pair_kernel, 64
+//      keys, a pair of waves per 32 keys (one computes P and dV, the other
+//      dS and dK);
 //   3. fa_bwd_dq_kernel: one workgroup owns 128 query rows (32 per wave) and
 //      streams 32-key tiles of K and V, like the forward kernel.
 // Splitting dQ from dK/dV computes S and dP twice (7 products instead of 5)
@@ -69,15 +71,6 @@ struct BwdCfg {
     __device__ static constexpr int swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 };
 
-// dK/dV kernel: NH 32-row query halves per streamed tile.  Two halves give
-// the MFMA pipe the second half's S and dP products while the first half's
-// exponentials run, but cost 32 more registers per half; at d = 128 the
-// non-causal kernel (which keeps more loop state) would spill with two.  The
-// d = 128 dV-only kernel takes one half and fits three workgroups per CU (160
-// VGPRs): measured 5-8 % faster over the whole backward call than two halves
-// at two workgroups per CU.
-enum KvMode { kBoth = 0, kOnlyDV = 1, kOnlyDK = 2 };
-
 // LDS operand reads kept in flight ahead of the MFMAs of the score phases
 // (S, dP) and of the accumulation phases (dV, dK, dQ); 0: the compiler's order.
 #ifndef FA_BWD_PF_S
@@ -87,15 +80,14 @@ enum KvMode { kBoth = 0, kOnlyDV = 1, kOnlyDK = 2 };
 #define FA_BWD_PF_V 3
 #endif
 
-#ifndef FA_BWD_SPLIT_DKV
-#define FA_BWD_SPLIT_DKV 1   // d = 128: dV and dK in two kernels (fewer registers each)
-#endif
-
-template <int D, bool CAUSAL, int MODE = kBoth>
+// dK/dV kernel in one wave per key (the d = 64 path): NH = 2 32-row query
+// halves per streamed tile give the MFMA pipe the second half's S and dP
+// products while the first half's exponentials run.
+template <int D>
 struct KvCfg {
     using C = BwdCfg<D>;
-    static constexpr int NH = (D == 128 && (MODE == kOnlyDK || MODE == kOnlyDV || (!CAUSAL && MODE == kBoth))) ? 1 : 2;
-    static constexpr int OCC = MODE == kOnlyDV ? 3 : MODE != kBoth ? 2 : (D == 128 ? 1 : 2);   // workgroups per CU
+    static constexpr int NH = 2;
+    static constexpr int OCC = 2;                 // workgroups per CU
     static constexpr int TQ = 32 * NH;            // query rows per streamed tile
     static constexpr int QSTAGE = 2 * TQ * D * 2; // Q tile + dO tile
     static constexpr int QTILES = 2 * QSTAGE;     // two stages
@@ -283,12 +275,11 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- 2. dK and dV
 
-template <int D, bool CAUSAL, int MODE, bool VARLEN>
-__global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv_kernel(BwdParams pin) {
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, KvCfg<D>::OCC) void fa_bwd_dkv_kernel(BwdParams pin) {
     BwdParams p = pin;
     using C = BwdCfg<D>;
-    using K = KvCfg<D, CAUSAL, MODE>;
-    constexpr bool DO_DV = MODE != kOnlyDK, DO_DK = MODE != kOnlyDV;
+    using K = KvCfg<D>;
     constexpr int NH = K::NH, TQ = K::TQ;
     __shared__ __attribute__((aligned(1024))) char smem_raw[K::LDS];
     lds_char* smem = (lds_char*)smem_raw;
@@ -329,9 +320,9 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
     }
     const int64_t kvbase = VARLEN ? k_tok0 * KVSTR + (int64_t)hkv * C::ROW
                                   : (int64_t)(b * p.Hkv + hkv) * p.Nk * C::ROW;
-    bf16x8 kf[C::KS], vf[DO_DK ? C::KS : 1];
+    bf16x8 kf[C::KS], vf[C::KS];
     load_b_rows<D>(reinterpret_cast<const char*>(p.k) + kvbase, key, p.Nk, g, kf, KVSTR);
-    if constexpr (DO_DK) load_b_rows<D>(reinterpret_cast<const char*>(p.v) + kvbase, key, p.Nk, g, vf, KVSTR);
+    load_b_rows<D>(reinterpret_cast<const char*>(p.v) + kvbase, key, p.Nk, g, vf, KVSTR);
 
     // query tiles to visit, per query head of the group
     const int qs = CAUSAL ? max(0, k0 - p.causal_shift) : 0;       // first query that sees key k0
@@ -381,11 +372,8 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
         for (int hh = 0; hh < NH; ++hh) scratch[(g ? TQ : 0) + 32 * hh + n] = pre[hh];
         const int qt = qt0 + (it % nqt);
         const int q0 = qt * TQ;
-        // No key of this wave is visible to these rows.  The dV-only kernel
-        // computes such tiles anyway (its mask zeroes them): the early exit
-        // made the compiler move its accumulators between registers and spill
-        // at three workgroups per CU.
-        if (MODE != kOnlyDV && q0 + TQ - 1 < wqs) {
+        // no key of this wave is visible to these rows
+        if (q0 + TQ - 1 < wqs) {
             if (it + 1 < n_it) issue(it + 1, STG ^ 1);
             return;
         }
@@ -403,11 +391,10 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
                 s[hh] = mfma_bf16_32x32x16(lds_b128(qb + 32 * hh * C::ROW + off.b[ks]), kf[ks], s[hh]);
-                if constexpr (DO_DK)
-                    dp[hh] = mfma_bf16_32x32x16(lds_b128(ob + 32 * hh * C::ROW + off.b[ks]), vf[ks], dp[hh]);
+                dp[hh] = mfma_bf16_32x32x16(lds_b128(ob + 32 * hh * C::ROW + off.b[ks]), vf[ks], dp[hh]);
             }
         }
-        order_reads_ahead<NH * C::KS * (DO_DK ? 2 : 1), 1, FA_BWD_PF_S>();
+        order_reads_ahead<NH * C::KS * 2, 1, FA_BWD_PF_S>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (it + 1 < n_it) issue(it + 1, STG ^ 1);
@@ -420,8 +407,7 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(scratch + 32 * hh + 8 * a + 4 * g);
-                f32x4 y = f32x4{};
-                if constexpr (DO_DK) y = *reinterpret_cast<const f32x4*>(scratch + TQ + 32 * hh + 8 * a + 4 * g);
+                const f32x4 y = *reinterpret_cast<const f32x4*>(scratch + TQ + 32 * hh + 8 * a + 4 * g);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     l2[4 * a + r] = x[r];
@@ -446,8 +432,8 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
 #pragma unroll
             for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (dp[hh][i] - dl[i]);
             bf16x8 pp[2], pd[2];
-            if constexpr (DO_DV) pack_b(pv, pp);
-            if constexpr (DO_DK) pack_b(ds, pd);
+            pack_b(pv, pp);
+            pack_b(ds, pd);
             const lds_char* qbh = qb + 32 * hh * C::ROW;
             const lds_char* obh = ob + 32 * hh * C::ROW;
             __builtin_amdgcn_sched_barrier(0);
@@ -456,10 +442,10 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
-                    if constexpr (DO_DV) dv[db] = mfma_bf16_32x32x16(tr_operand<D>(obh, off, db, st), pp[st], dv[db]);
-                    if constexpr (DO_DK) dk[db] = mfma_bf16_32x32x16(tr_operand<D>(qbh, off, db, st), pd[st], dk[db]);
+                    dv[db] = mfma_bf16_32x32x16(tr_operand<D>(obh, off, db, st), pp[st], dv[db]);
+                    dk[db] = mfma_bf16_32x32x16(tr_operand<D>(qbh, off, db, st), pd[st], dk[db]);
                 }
-            order_reads_ahead<2 * C::DB * ((DO_DV ? 1 : 0) + (DO_DK ? 1 : 0)), 2, FA_BWD_PF_V>();
+            order_reads_ahead<2 * C::DB * 2, 2, FA_BWD_PF_V>();
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(0);
         }
@@ -473,8 +459,205 @@ __global__ __launch_bounds__(256, (KvCfg<D, CAUSAL, MODE>::OCC)) void fa_bwd_dkv
 
     char* dK = reinterpret_cast<char*>(p.dk) + kvbase;
     char* dV = reinterpret_cast<char*>(p.dv) + kvbase;
-    if constexpr (DO_DK) store_rows<D>(smem, dk, p.scale, dK, k0, p.Nk, w, n, g, lane, KVSTR);
-    if constexpr (DO_DV) store_rows<D>(smem, dv, 1.f, dV, k0, p.Nk, w, n, g, lane, KVSTR);
+    store_rows<D>(smem, dk, p.scale, dK, k0, p.Nk, w, n, g, lane, KVSTR);
+    store_rows<D>(smem, dv, 1.f, dV, k0, p.Nk, w, n, g, lane, KVSTR);
+}
+
+// ---------------------------------------------------------------- 2b. dK and dV by wave pairs (d = 128)
+
+// The work of one key split over a pair of waves.  The P wave holds the key's
+// K row and computes S = Q K^T, P and dV^T += dO^T P; the dS wave holds its V
+// row and computes dP = dO V^T, takes P from the P wave through LDS, and
+// forms dS = P (dP - D) and dK^T += Q^T dS.  That is four products per key and
+// query tile, as in the one-wave kernel above, but each wave keeps one
+// operand and one accumulator, so three workgroups fit per CU at d = 128
+// (the one-wave kernel needs 474 registers there).  A workgroup owns 64
+// keys: waves 0 and 1 are the P waves of keys 0-31 and 32-63, waves 2 and 3
+// the dS waves of the same keys.  A second barrier per tile publishes P.
+template <int D>
+struct PairCfg {
+    using C = BwdCfg<D>;
+    static constexpr int KEYS = 64;                    // keys per workgroup
+    static constexpr int TQ = 32;                      // query rows per streamed tile
+    static constexpr int QSTAGE = 2 * TQ * C::ROW;     // Q tile + dO tile
+    static constexpr int QTILES = 2 * QSTAGE;          // two stages
+    static constexpr int PX = 2 * 32 * 32 * 4;         // P of both pairs, fp32
+    static constexpr int SCRATCH = 4 * TQ * C::NW;     // per wave: one row statistic of the tile
+    static constexpr int LDS = QTILES + PX + SCRATCH > C::OUT ? QTILES + PX + SCRATCH : C::OUT;
+};
+
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, 3) void fa_bwd_dkv_pair_kernel(BwdParams pin) {
+    BwdParams p = pin;
+    using C = BwdCfg<D>;
+    using K = PairCfg<D>;
+    constexpr int TQ = K::TQ;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[K::LDS];
+    lds_char* smem = (lds_char*)smem_raw;
+    const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int g = lane >> 5;
+    const bool dsw = w >= 2;                     // dS wave (else P wave)
+    const int pr = w & 1;                        // pair: keys 32 pr .. 32 pr + 31 of the workgroup
+
+    // workgroup -> (batch, key/value head, key tile), as in fa_bwd_dkv_kernel
+    int b, hkv, kt;
+    if (VARLEN && p.compact_dkv) {
+        const int k = blockIdx.x / p.Hkv;
+        hkv = blockIdx.x - k * p.Hkv;
+        if (!varlen_slot<false>(p.cu_k, p.total_k, p.B, p.n_ktiles, K::KEYS, k, b, kt)) return;
+        b = __builtin_amdgcn_readfirstlane(b);
+        kt = __builtin_amdgcn_readfirstlane(kt);
+    } else {
+        int kvflat, unused;
+        bwd_order(blockIdx.x, p.B * p.Hkv, 1, p.n_ktiles, p.group_dkv, kvflat, unused, kt);
+        b = kvflat / p.Hkv;
+        hkv = kvflat - b * p.Hkv;
+    }
+    const int k0 = kt * K::KEYS;
+    const int wk0 = k0 + 32 * pr;
+    const int key = wk0 + n;
+
+    const int64_t QSTR = VARLEN ? (int64_t)p.Hq * C::ROW : C::ROW;
+    const int64_t KVSTR = VARLEN ? (int64_t)p.Hkv * C::ROW : C::ROW;
+    int64_t q_tok0 = 0, k_tok0 = 0;
+    if constexpr (VARLEN) {
+        seq_bounds(p, b, q_tok0, k_tok0);
+        if (k0 >= p.Nk) return;                  // past this sequence's keys: nothing to write
+    }
+    const int64_t kvbase = VARLEN ? k_tok0 * KVSTR + (int64_t)hkv * C::ROW
+                                  : (int64_t)(b * p.Hkv + hkv) * p.Nk * C::ROW;
+    // B operand of the first product: K rows (P wave) or V rows (dS wave)
+    bf16x8 rf[C::KS];
+    load_b_rows<D>(reinterpret_cast<const char*>(dsw ? p.v : p.k) + kvbase, key, p.Nk, g, rf, KVSTR);
+
+    const int qs = CAUSAL ? max(0, k0 - p.causal_shift) : 0;       // first query that sees key k0
+    const int qt0 = qs / TQ;
+    const int nqt = qs < p.Nq ? (p.Nq + TQ - 1) / TQ - qt0 : 0;
+    const int n_it = __builtin_amdgcn_readfirstlane(nqt * p.group);
+    const int64_t R = VARLEN ? (int64_t)p.Hq * p.total_q : (int64_t)p.B * p.Hq * p.Nq;
+
+    const TileOffsets<D> off(n, g);
+    float* scratch = reinterpret_cast<float*>(smem_raw + K::QTILES + K::PX + w * 4 * TQ);
+    float* px = reinterpret_cast<float*>(smem_raw + K::QTILES) + pr * 1024;   // this pair's P
+
+    f32x16 acc[C::DB];                           // dV^T (P wave) or dK^T (dS wave)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+    // the statistic each wave needs: base-2 LSE (P wave) or D (dS wave)
+    const int64_t stat = dsw ? 0 : R;
+    float pre;
+    auto issue = [&](int it, int stage) {
+        const int gi = it / nqt;
+        const int qt = qt0 + (it - gi * nqt);
+        const int h = hkv * p.group + gi;
+        const int64_t qbase = VARLEN ? q_tok0 * QSTR + (int64_t)h * C::ROW : (int64_t)(b * p.Hq + h) * p.Nq * C::ROW;
+        const int64_t wrow0 = VARLEN ? (int64_t)h * p.total_q + q_tok0 : (int64_t)(b * p.Hq + h) * p.Nq;
+        copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qbase,
+                         reinterpret_cast<const char*>(p.dout) + qbase, qt * TQ, p.Nq,
+                         smem_u32 + stage * K::QSTAGE, w, lane, QSTR);
+        pre = p.ws[stat + wrow0 + min(qt * TQ + n, p.Nq - 1)];
+    };
+
+    // The role is a template argument: each role runs a loop of its own, so
+    // the registers of one role's values are not held live in the other's.
+    auto tile = [&](auto stage_c, auto role_c, int it) {
+        constexpr int STG = decltype(stage_c)::value;
+        constexpr bool DSW = decltype(role_c)::value;
+        FA_WAIT_VMCNT(0);
+        bwd_barrier();
+        scratch[n] = pre;                        // both lane halves write the same value of row n
+        const int q0 = (qt0 + (it % nqt)) * TQ;
+        const lds_char* qb = smem + STG * K::QSTAGE;
+        const lds_char* ob = qb + TQ * C::ROW;
+        f32x16 s = f32x16{};                     // S (P wave) or dP (dS wave)
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) s = mfma_bf16_32x32x16(lds_b128((DSW ? ob : qb) + off.b[ks]), rf[ks], s);
+        order_reads_ahead<C::KS, 1, FA_BWD_PF_S>();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        if (it + 1 < n_it) issue(it + 1, STG ^ 1);
+
+        // element i of a lane holds query row q0 + 8*(i/4) + 4g + i%4 and key `key`
+        bf16x8 pk[2];                            // P (P wave) or dS (dS wave) as B operands
+        if constexpr (!DSW) {
+            float l2[16];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(scratch + 8 * a + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) l2[4 * a + r] = x[r];
+            }
+            f32x16 pv;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(fmaf(s[i], p.c, -l2[i]));
+            const bool need_mask = (q0 + 32 > p.Nq) || (CAUSAL && wk0 + 31 > q0 + p.causal_shift);
+            if (need_mask) {
+                // rows past Nq, and (causal) rows before the first one this
+                // lane's key is visible to
+                const int hi = p.Nq - q0 - 4 * g;
+                const int lo = CAUSAL ? key - p.causal_shift - q0 - 4 * g : 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int idx = 8 * (i >> 2) + (i & 3);
+                    pv[i] = (idx >= hi || idx < lo) ? 0.f : pv[i];
+                }
+            }
+            // lane-major 16-byte pieces: conflict-free, and the dS wave's lane
+            // reads back exactly what the same lane of the P wave wrote
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(px + j * 256 + lane * 4) = f32x4{pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]};
+            pack_b(pv, pk);
+        }
+        bwd_barrier();                           // P of the tile is in LDS
+        if constexpr (DSW) {
+            f32x16 ds;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 dl = *reinterpret_cast<const f32x4*>(scratch + 8 * a + 4 * g);
+                const f32x4 pv = *reinterpret_cast<const f32x4*>(px + a * 256 + lane * 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ds[4 * a + r] = pv[r] * (s[4 * a + r] - dl[r]);
+            }
+            pack_b(ds, pk);
+        }
+        // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave)
+        const lds_char* tb = DSW ? qb : ob;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+                acc[db] = mfma_bf16_32x32x16(tr_operand<D>(tb, off, db, st), pk[st], acc[db]);
+        order_reads_ahead<2 * C::DB, 2, FA_BWD_PF_V>();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    auto run = [&](auto role_c) {
+        if (n_it > 0) issue(0, 0);
+        for (int it = 0; it < n_it; it += 2) {
+            tile(std::integral_constant<int, 0>{}, role_c, it);
+            if (it + 1 < n_it) tile(std::integral_constant<int, 1>{}, role_c, it + 1);
+        }
+    };
+    if (dsw)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
+
+    // P waves write dV, dS waves dK (scaled); store_rows stages wave w's rows
+    // at 32 w, so the dS waves' rows start 64 below their keys
+    char* dst = reinterpret_cast<char*>(dsw ? p.dk : p.dv) + kvbase;
+    store_rows<D>(smem, acc, dsw ? p.scale : 1.f, dst, dsw ? k0 - 64 : k0, p.Nk, w, n, g, lane, KVSTR);
 }
 
 // ---------------------------------------------------------------- 3. dQ
@@ -632,21 +815,21 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     // sequence's end return at once.  A packed batch whose padded grid would
     // be 8 times the tiles that exist takes the compact grid instead
     // (varlen_compact in fa_varlen.hpp).
-    pp.n_ktiles = (p.Nk + C::ROWS - 1) / C::ROWS;
-    pp.compact_dkv = VARLEN && varlen_compact(p.total_k, p.B, pp.n_ktiles, C::ROWS) ? 1 : 0;
-    const int64_t kv_grid = pp.compact_dkv ? varlen_slots(p.total_k, p.B, pp.n_ktiles, C::ROWS) * p.Hkv
+    // d = 128: wave pairs, 64 keys per workgroup; d = 64: one wave per key
+    constexpr bool PAIR = D == 128;
+    constexpr int KV_ROWS = PAIR ? PairCfg<D>::KEYS : C::ROWS;
+    pp.n_ktiles = (p.Nk + KV_ROWS - 1) / KV_ROWS;
+    pp.compact_dkv = VARLEN && varlen_compact(p.total_k, p.B, pp.n_ktiles, KV_ROWS) ? 1 : 0;
+    const int64_t kv_grid = pp.compact_dkv ? varlen_slots(p.total_k, p.B, pp.n_ktiles, KV_ROWS) * p.Hkv
                                            : (int64_t)pp.n_ktiles * p.B * p.Hkv;
     if (kv_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if (kv_grid > 0) {
-        if constexpr (FA_BWD_SPLIT_DKV && D == 128) {
-            const void* kdv = reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDV, VARLEN>);
-            e = hipLaunchKernel(kdv, dim3((unsigned)kv_grid), dim3(256), args, test_extra_lds(KvCfg<D, CAUSAL, kOnlyDV>::LDS), stream);
-            if (e != hipSuccess) return e;
-            const void* kdk = reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kOnlyDK, VARLEN>);
-            e = hipLaunchKernel(kdk, dim3((unsigned)kv_grid), dim3(256), args, test_extra_lds(KvCfg<D, CAUSAL, kOnlyDK>::LDS), stream);
+        if constexpr (PAIR) {
+            const void* kpair = reinterpret_cast<const void*>(&fa_bwd_dkv_pair_kernel<D, CAUSAL, VARLEN>);
+            e = hipLaunchKernel(kpair, dim3((unsigned)kv_grid), dim3(256), args, test_extra_lds(PairCfg<D>::LDS), stream);
         } else {
-            const void* kboth = reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, kBoth, VARLEN>);
-            e = hipLaunchKernel(kboth, dim3((unsigned)kv_grid), dim3(256), args, test_extra_lds(KvCfg<D, CAUSAL, kBoth>::LDS), stream);
+            const void* kboth = reinterpret_cast<const void*>(&fa_bwd_dkv_kernel<D, CAUSAL, VARLEN>);
+            e = hipLaunchKernel(kboth, dim3((unsigned)kv_grid), dim3(256), args, test_extra_lds(KvCfg<D>::LDS), stream);
         }
         if (e != hipSuccess) return e;
     }
