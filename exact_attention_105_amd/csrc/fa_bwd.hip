@@ -35,7 +35,8 @@
 //                                   registers; lane = key)
 //     dV^T += dO^T P, dK^T += Q^T dS   (A: transposing LDS reads of dO / Q)
 // Tiles are copied straight into LDS (global_load_lds_dwordx4), two stages,
-// XOR-swizzled in 16-byte units so the ds_read_b128 reads are conflict-free.
+// XOR-swizzled in 16-byte units so that both the ds_read_b128 row reads and the
+// transposing reads are conflict-free (BwdCfg::swz).
 #include <algorithm>
 #include <type_traits>
 
@@ -64,11 +65,22 @@ struct BwdCfg {
     static constexpr int OUT = ROWS * ROW;        // epilogue staging of 128 output rows
     static constexpr int LDS = TILES > OUT ? TILES : OUT;                       // dQ kernel
     static constexpr int RPC = 1024 / ROW;        // rows per 1 KiB copy
-    // 16-byte-unit XOR swizzle of LDS rows: the 16 rows one ds_read_b128
-    // cycle touches cover all units (row mod 16 for 256-byte rows, (row/2)
-    // mod 8 for 128-byte rows, two of which share a bank sweep).  It is
+    // 16-byte-unit XOR swizzle of LDS rows.  The tiles are read both as rows
+    // (ds_read_b128: 16 lanes per cycle on 16 consecutive rows) and
+    // transposed (ds_read_b64_tr_b16: 32 lanes per cycle on 4 rows, 4 units
+    // each), and the swizzle keeps both patterns on distinct banks:
+    //   256-byte rows: bits 2-3 = row mod 4 move the 4 rows of a transposed
+    //     read to different 64-byte bank groups, bits 0-1 = (row / 4) mod 4
+    //     complete a permutation of 16 consecutive rows;
+    //   128-byte rows (two share a bank sweep): bit 2 = (row / 2) mod 2,
+    //     bits 0-1 = (row / 4) mod 4, a permutation of the 8 rows of one
+    //     parity in 16.
+    // (row mod 16 alone, the plain row swizzle, put the 4 rows of a
+    // transposed read into one bank group: a 4-way conflict.)  It is
     // unchanged by a step of 16 rows.
-    __device__ static constexpr int swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+    __device__ static constexpr int swz(int row) {
+        return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+    }
 };
 
 // LDS operand reads kept in flight ahead of the MFMAs of the score phases
