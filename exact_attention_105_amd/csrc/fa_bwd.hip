@@ -287,6 +287,34 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- 2. dK and dV
 
+// The query tiles a dK/dV workgroup streams, in order: for each query head
+// hkv*group + gi of the group, query tiles qt0 .. qt0 + nqt - 1.  The walk
+// keeps the tile index within the head and the head's first row (bytes into
+// q / dO, index into the workspace) and advances them by one tile per call
+// of next(), instead of dividing the tile counter by nqt each time.
+struct QueryWalk {
+    int iq = 0;               // query tile qt0 + iq of the current head
+    int nqt;
+    int64_t qbase, wrow0;     // the current head's first row: bytes into q / dO, workspace index
+    int64_t head_bytes, head_rows;
+    __device__ QueryWalk(const BwdParams& p, int b, int hkv, int64_t q_tok0, int nqt_, bool varlen, int row_bytes)
+        : nqt(nqt_) {
+        const int h = hkv * p.group;
+        const int64_t qstr = varlen ? (int64_t)p.Hq * row_bytes : row_bytes;
+        qbase = varlen ? q_tok0 * qstr + (int64_t)h * row_bytes : (int64_t)(b * p.Hq + h) * p.Nq * row_bytes;
+        wrow0 = varlen ? (int64_t)h * p.total_q + q_tok0 : (int64_t)(b * p.Hq + h) * p.Nq;
+        head_bytes = varlen ? (int64_t)row_bytes : (int64_t)p.Nq * row_bytes;
+        head_rows = varlen ? (int64_t)p.total_q : (int64_t)p.Nq;
+    }
+    __device__ void next() {
+        if (++iq == nqt) {
+            iq = 0;
+            qbase += head_bytes;
+            wrow0 += head_rows;
+        }
+    }
+};
+
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, KvCfg<D>::OCC) void fa_bwd_dkv_kernel(BwdParams pin) {
     BwdParams p = pin;
@@ -358,22 +386,20 @@ __global__ __launch_bounds__(256, KvCfg<D>::OCC) void fa_bwd_dkv_kernel(BwdParam
     // Its copies go to LDS; the row statistics of its TQ rows to `pre`
     // (pre[h]: lanes 0-31 the base-2 LSE of row 32h + n, lanes 32-63 its D).
     float pre[NH];
-    auto issue = [&](int it, int stage) {
-        const int gi = it / nqt;
-        const int qt = qt0 + (it - gi * nqt);
-        const int h = hkv * p.group + gi;
-        // first row of head h: bytes into q / dO, and its index into the workspace
-        const int64_t qbase = VARLEN ? q_tok0 * QSTR + (int64_t)h * C::ROW : (int64_t)(b * p.Hq + h) * p.Nq * C::ROW;
-        const int64_t wrow0 = VARLEN ? (int64_t)h * p.total_q + q_tok0 : (int64_t)(b * p.Hq + h) * p.Nq;
-        copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qbase,
-                         reinterpret_cast<const char*>(p.dout) + qbase, qt * TQ, p.Nq,
+    QueryWalk qw(p, b, hkv, q_tok0, nqt, VARLEN, C::ROW);
+    auto issue = [&](int stage) {
+        const int qt = qt0 + qw.iq;
+        copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qw.qbase,
+                         reinterpret_cast<const char*>(p.dout) + qw.qbase, qt * TQ, p.Nq,
                          smem_u32 + stage * K::QSTAGE, w, lane, QSTR);
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
             const int r = min(qt * TQ + 32 * hh + n, p.Nq - 1);
-            pre[hh] = p.ws[(g ? 0 : R) + wrow0 + r];
+            pre[hh] = p.ws[(g ? 0 : R) + qw.wrow0 + r];
         }
+        qw.next();
     };
+    int cur_q = 0;                               // the computed tile is query tile qt0 + cur_q
 
     auto tile = [&](auto stage_c, int it) {
         constexpr int STG = decltype(stage_c)::value;
@@ -382,11 +408,11 @@ __global__ __launch_bounds__(256, KvCfg<D>::OCC) void fa_bwd_dkv_kernel(BwdParam
         // scratch: [0, TQ) base-2 LSE, [TQ, 2 TQ) D of the tile's rows
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) scratch[(g ? TQ : 0) + 32 * hh + n] = pre[hh];
-        const int qt = qt0 + (it % nqt);
-        const int q0 = qt * TQ;
+        const int q0 = (qt0 + cur_q) * TQ;
+        if (++cur_q == nqt) cur_q = 0;
         // no key of this wave is visible to these rows
         if (q0 + TQ - 1 < wqs) {
-            if (it + 1 < n_it) issue(it + 1, STG ^ 1);
+            if (it + 1 < n_it) issue(STG ^ 1);
             return;
         }
         const lds_char* qb = smem + STG * K::QSTAGE;
@@ -409,7 +435,7 @@ __global__ __launch_bounds__(256, KvCfg<D>::OCC) void fa_bwd_dkv_kernel(BwdParam
         order_reads_ahead<NH * C::KS * 2, 1, FA_BWD_PF_S>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
-        if (it + 1 < n_it) issue(it + 1, STG ^ 1);
+        if (it + 1 < n_it) issue(STG ^ 1);
 
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
@@ -463,7 +489,7 @@ __global__ __launch_bounds__(256, KvCfg<D>::OCC) void fa_bwd_dkv_kernel(BwdParam
         }
     };
 
-    if (n_it > 0) issue(0, 0);
+    if (n_it > 0) issue(0);
     for (int it = 0; it < n_it; it += 2) {
         tile(std::integral_constant<int, 0>{}, it);
         if (it + 1 < n_it) tile(std::integral_constant<int, 1>{}, it + 1);
@@ -563,17 +589,16 @@ __global__ __launch_bounds__(256, 3) void fa_bwd_dkv_pair_kernel(BwdParams pin) 
     // the statistic each wave needs: base-2 LSE (P wave) or D (dS wave)
     const int64_t stat = dsw ? 0 : R;
     float pre;
-    auto issue = [&](int it, int stage) {
-        const int gi = it / nqt;
-        const int qt = qt0 + (it - gi * nqt);
-        const int h = hkv * p.group + gi;
-        const int64_t qbase = VARLEN ? q_tok0 * QSTR + (int64_t)h * C::ROW : (int64_t)(b * p.Hq + h) * p.Nq * C::ROW;
-        const int64_t wrow0 = VARLEN ? (int64_t)h * p.total_q + q_tok0 : (int64_t)(b * p.Hq + h) * p.Nq;
-        copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qbase,
-                         reinterpret_cast<const char*>(p.dout) + qbase, qt * TQ, p.Nq,
+    QueryWalk qw(p, b, hkv, q_tok0, nqt, VARLEN, C::ROW);
+    auto issue = [&](int stage) {
+        const int qt = qt0 + qw.iq;
+        copy_pair<D, TQ>(reinterpret_cast<const char*>(p.q) + qw.qbase,
+                         reinterpret_cast<const char*>(p.dout) + qw.qbase, qt * TQ, p.Nq,
                          smem_u32 + stage * K::QSTAGE, w, lane, QSTR);
-        pre = p.ws[stat + wrow0 + min(qt * TQ + n, p.Nq - 1)];
+        pre = p.ws[stat + qw.wrow0 + min(qt * TQ + n, p.Nq - 1)];
+        qw.next();
     };
+    int cur_q = 0;                               // the computed tile is query tile qt0 + cur_q
 
     // The role is a template argument: each role runs a loop of its own, so
     // the registers of one role's values are not held live in the other's.
@@ -583,7 +608,8 @@ __global__ __launch_bounds__(256, 3) void fa_bwd_dkv_pair_kernel(BwdParams pin) 
         FA_WAIT_VMCNT(0);
         bwd_barrier();
         scratch[n] = pre;                        // both lane halves write the same value of row n
-        const int q0 = (qt0 + (it % nqt)) * TQ;
+        const int q0 = (qt0 + cur_q) * TQ;
+        if (++cur_q == nqt) cur_q = 0;
         const lds_char* qb = smem + STG * K::QSTAGE;
         const lds_char* ob = qb + TQ * C::ROW;
         f32x16 s = f32x16{};                     // S (P wave) or dP (dS wave)
@@ -594,7 +620,7 @@ __global__ __launch_bounds__(256, 3) void fa_bwd_dkv_pair_kernel(BwdParams pin) 
         order_reads_ahead<C::KS, 1, FA_BWD_PF_S>();
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
-        if (it + 1 < n_it) issue(it + 1, STG ^ 1);
+        if (it + 1 < n_it) issue(STG ^ 1);
 
         // element i of a lane holds query row q0 + 8*(i/4) + 4g + i%4 and key `key`
         bf16x8 pk[2];                            // P (P wave) or dS (dS wave) as B operands
@@ -655,7 +681,7 @@ __global__ __launch_bounds__(256, 3) void fa_bwd_dkv_pair_kernel(BwdParams pin) 
     };
 
     auto run = [&](auto role_c) {
-        if (n_it > 0) issue(0, 0);
+        if (n_it > 0) issue(0);
         for (int it = 0; it < n_it; it += 2) {
             tile(std::integral_constant<int, 0>{}, role_c, it);
             if (it + 1 < n_it) tile(std::integral_constant<int, 1>{}, role_c, it + 1);
