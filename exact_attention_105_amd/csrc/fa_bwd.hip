@@ -800,14 +800,18 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams pin) {
         if (j + 1 < n_tiles) issue(j + 1, STG ^ 1);
 
         const bool need_mask = (key0 + C::T > p.Nk) || (CAUSAL && key0 + C::T - 1 > wq0 + p.causal_shift);
-        const int lim = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - key0 - 4 * g;
-        f32x16 ds;
+        f32x16 pv, ds;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float e = fast_exp2(fmaf(s[i], p.c, -lse2));
-            if (need_mask && 8 * (i >> 2) + (i & 3) > lim) e = 0.f;
-            ds[i] = e * (dp[i] - dlt);
+        for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(fmaf(s[i], p.c, -lse2));
+        // Only edge tiles mask (a wave-uniform branch); folded into every
+        // element's arithmetic, the test cost two VALU instructions per score.
+        if (need_mask) {
+            const int lim = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - key0 - 4 * g;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) pv[i] = 8 * (i >> 2) + (i & 3) > lim ? 0.f : pv[i];
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (dp[i] - dlt);
         bf16x8 pd[2];
         pack_b(ds, pd);
         __builtin_amdgcn_sched_barrier(0);
