@@ -72,7 +72,7 @@ def build(verbose: bool = False, jobs: int = 4, extra_flags=(), out: str = LIB,
 
 
 MICROBENCH = os.path.join(PKG, "microbench")
-MICROBENCH_SOURCES = ["issue_rates.hip", "fp8_accumulation.hip", "coexec.hip", "phases.hip"]
+MICROBENCH_SOURCES = ["issue_rates.hip", "fp8_accumulation.hip", "coexec.hip", "phases.hip", "read_bw.hip"]
 
 
 def build_microbench(verbose: bool = False) -> list:
