@@ -18,8 +18,10 @@
 //      128 keys, one wave per 32 keys; d = 128: fa_bwd_dkv_pair_kernel, 64
 //      keys, a pair of waves per 32 keys (one computes P and dV, the other
 //      dS and dK);
-//   3. fa_bwd_dq_kernel: one workgroup owns 128 query rows (32 per wave) and
-//      streams 32-key tiles of K and V, like the forward kernel.
+//   3. dQ: one workgroup owns 128 query rows (32 per wave) and streams
+//      32-key tiles of K and V, like the forward kernel (fa_bwd_dq_kernel;
+//      at d = 128 fa_bwd_dq_pipe_kernel, which issues the next tile's score
+//      products during the current tile's softmax).
 // Splitting dQ from dK/dV computes S and dP twice (7 products instead of 5)
 // but needs neither a float workspace for dQ nor atomics.
 //
@@ -90,6 +92,9 @@ struct BwdCfg {
 #endif
 #ifndef FA_BWD_PF_V
 #define FA_BWD_PF_V 3
+#endif
+#ifndef FA_BWD_DQ_PIPE
+#define FA_BWD_DQ_PIPE 1     // d = 128: dQ with the key loop software-pipelined
 #endif
 
 // dK/dV kernel in one wave per key (the d = 64 path): NH = 2 32-row query
@@ -834,6 +839,172 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams pin) {
     store_rows<D>(smem, acc, p.scale, reinterpret_cast<char*>(p.dq) + qbase, q0, p.Nq, w, n, g, lane, QSTR);
 }
 
+// dQ with the key loop software-pipelined: the S^T and dP^T products of key
+// tile j + 1 are issued in the same instruction stream as the softmax of
+// tile j, so a wave keeps the MFMA pipe busy through its own exponentials.
+// At two waves per SIMD (the dQ kernel's occupancy either way) the registers
+// for the second pair of score blocks are free.  Three LDS stages: tile j
+// (read by the dQ product), j + 1 (read by the score products) and j + 2
+// (copies in flight).  Every wave computes every tile of the workgroup; the
+// mask zeroes the scores of keys hidden from its rows.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq_pipe_kernel(BwdParams pin) {
+    BwdParams p = pin;
+    using C = BwdCfg<D>;
+    constexpr int NST = 3;
+    constexpr int LDS = NST * C::STAGE > C::OUT ? NST * C::STAGE : C::OUT;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[LDS];
+    lds_char* smem = (lds_char*)smem_raw;
+    const uint32_t smem_u32 = (uint32_t)(uintptr_t)smem;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;
+    const int g = lane >> 5;
+
+    int b, hkv, hq, qt;
+    if (VARLEN && p.compact_dq) {
+        const int k = blockIdx.x / p.Hq;
+        const int x = blockIdx.x - k * p.Hq;
+        hkv = x % p.Hkv;
+        hq = hkv * p.group + x / p.Hkv;
+        if (!varlen_slot<true>(p.cu_q, p.total_q, p.B, p.n_qtiles, C::ROWS, k, b, qt)) return;
+        b = __builtin_amdgcn_readfirstlane(b);
+        qt = __builtin_amdgcn_readfirstlane(qt);
+    } else {
+        int t_ord, kvflat, gi;
+        bwd_order(blockIdx.x, p.B * p.Hkv, p.group, p.n_qtiles, p.group_dq, kvflat, gi, t_ord);
+        b = kvflat / p.Hkv;
+        hkv = kvflat - b * p.Hkv;
+        hq = hkv * p.group + gi;
+        qt = CAUSAL ? p.n_qtiles - 1 - t_ord : t_ord;
+    }
+    const int q0 = qt * C::ROWS;
+    const int wq0 = q0 + 32 * w;
+    const int qrow = wq0 + n;
+
+    const int64_t QSTR = VARLEN ? (int64_t)p.Hq * C::ROW : C::ROW;
+    const int64_t KVSTR = VARLEN ? (int64_t)p.Hkv * C::ROW : C::ROW;
+    int64_t q_tok0 = 0, k_tok0 = 0;
+    if constexpr (VARLEN) {
+        seq_bounds(p, b, q_tok0, k_tok0);
+        if (q0 >= p.Nq) return;
+    }
+    const int64_t qbase = VARLEN ? q_tok0 * QSTR + (int64_t)hq * C::ROW : (int64_t)(b * p.Hq + hq) * p.Nq * C::ROW;
+    const int64_t kvbase = VARLEN ? k_tok0 * KVSTR + (int64_t)hkv * C::ROW
+                                  : (int64_t)(b * p.Hkv + hkv) * p.Nk * C::ROW;
+    const int64_t wrow0 = VARLEN ? (int64_t)hq * p.total_q + q_tok0 : (int64_t)(b * p.Hq + hq) * p.Nq;
+    const char* Kh = reinterpret_cast<const char*>(p.k) + kvbase;
+    const char* Vh = reinterpret_cast<const char*>(p.v) + kvbase;
+
+    const int kend = key_end(q0, C::ROWS, p.Nk, p.causal_shift, CAUSAL);
+    const int n_tiles = __builtin_amdgcn_readfirstlane((kend + C::T - 1) / C::T);
+
+    bf16x8 qf[C::KS], df[C::KS];
+    load_b_rows<D>(reinterpret_cast<const char*>(p.q) + qbase, qrow, p.Nq, g, qf, QSTR);
+    load_b_rows<D>(reinterpret_cast<const char*>(p.dout) + qbase, qrow, p.Nq, g, df, QSTR);
+    const int64_t R = VARLEN ? (int64_t)p.Hq * p.total_q : (int64_t)p.B * p.Hq * p.Nq;
+    float lse2 = INFINITY, dlt = 0.f;
+    if (qrow < p.Nq) {
+        dlt = p.ws[wrow0 + qrow];
+        lse2 = p.ws[R + wrow0 + qrow];
+    }
+    // last key visible to this lane's row, relative to element 0 of a tile
+    const int lim0 = (CAUSAL ? min(qrow + p.causal_shift, p.Nk - 1) : p.Nk - 1) - 4 * g;
+
+    const TileOffsets<D> off(n, g);
+    f32x16 acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+    auto issue = [&](int j, int stage) {
+        copy_pair<D, C::T>(Kh, Vh, j * C::T, p.Nk, smem_u32 + stage * C::STAGE, w, lane, KVSTR);
+    };
+    // S^T and dP^T of the tile in `stage`
+    auto scores = [&](int stage, f32x16& s, f32x16& dp) {
+        const lds_char* kb = smem + stage * C::STAGE;
+        const lds_char* vb = kb + C::TILE;
+        s = f32x16{};
+        dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            s = mfma_bf16_32x32x16(lds_b128(kb + off.b[ks]), qf[ks], s);
+            dp = mfma_bf16_32x32x16(lds_b128(vb + off.b[ks]), df[ks], dp);
+        }
+    };
+
+    f32x16 s0, dp0;
+    if (n_tiles > 0) {
+        issue(0, 0);
+        if (n_tiles > 1) issue(1, 1);
+        FA_WAIT_VMCNT(0);
+        bwd_barrier();
+        __builtin_amdgcn_s_setprio(1);
+        scores(0, s0, dp0);
+        __builtin_amdgcn_s_setprio(0);
+    }
+
+    // Tile j sits in stage U = j % 3 (compile time); its scores are in (s, dp).
+    auto tile = [&](auto u_c, int j) {
+        constexpr int U = decltype(u_c)::value;
+        constexpr int NXT = (U + 1) % NST, ISS = (U + 2) % NST;
+        // tile j + 1 landed; every wave is past tile j - 1, whose stage the
+        // copies of tile j + 2 now overwrite
+        FA_WAIT_VMCNT(0);
+        bwd_barrier();
+        if (j + 2 < n_tiles) issue(j + 2, ISS);
+        const int key0 = j * C::T;
+        const bool need_mask = (key0 + C::T > p.Nk) || (CAUSAL && key0 + C::T - 1 > wq0 + p.causal_shift);
+        // One basic block: the score products of tile j + 1 (for the last
+        // tile they read a stale stage and are discarded) interleaved with
+        // the softmax of tile j, one MFMA, one LDS read and four VALU
+        // instructions at a time.  The mask comes after, on dS, so that no
+        // branch splits the block.
+        f32x16 s1, dp1, pv, ds;
+        __builtin_amdgcn_sched_barrier(0);
+        scores(NXT, s1, dp1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pv[i] = fast_exp2(fmaf(s0[i], p.c, -lse2));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = pv[i] * (dp0[i] - dlt);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int m = 0; m < 2 * C::KS; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m + 2 < 2 * C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 64 / (2 * C::KS), 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (need_mask) {
+            const int lim = lim0 - key0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ds[i] = 8 * (i >> 2) + (i & 3) > lim ? 0.f : ds[i];
+        }
+        bf16x8 pd[2];
+        pack_b(ds, pd);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        const lds_char* kb = smem + U * C::STAGE;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) acc[db] = mfma_bf16_32x32x16(tr_operand<D>(kb, off, db, st), pd[st], acc[db]);
+        order_reads_ahead<2 * C::DB, 2, FA_BWD_PF_V>();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        s0 = s1;
+        dp0 = dp1;
+    };
+
+    for (int j = 0; j < n_tiles; j += NST) {
+        tile(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, j + 1);
+        if (j + 2 < n_tiles) tile(std::integral_constant<int, 2>{}, j + 2);
+    }
+
+    store_rows<D>(smem, acc, p.scale, reinterpret_cast<char*>(p.dq) + qbase, q0, p.Nq, w, n, g, lane, QSTR);
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     using C = BwdCfg<D>;
@@ -881,8 +1052,13 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
                                          : (int64_t)pp.n_qtiles * p.B * p.Hq;
     if (q_grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if (q_grid > 0) {
-        const void* kdq = reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, VARLEN>);
-        e = hipLaunchKernel(kdq, dim3((unsigned)q_grid), dim3(256), args, test_extra_lds(C::LDS), stream);
+        if constexpr (FA_BWD_DQ_PIPE && D == 128) {
+            const void* kdq = reinterpret_cast<const void*>(&fa_bwd_dq_pipe_kernel<D, CAUSAL, VARLEN>);
+            e = hipLaunchKernel(kdq, dim3((unsigned)q_grid), dim3(256), args, test_extra_lds(3 * C::STAGE), stream);
+        } else {
+            const void* kdq = reinterpret_cast<const void*>(&fa_bwd_dq_kernel<D, CAUSAL, VARLEN>);
+            e = hipLaunchKernel(kdq, dim3((unsigned)q_grid), dim3(256), args, test_extra_lds(C::LDS), stream);
+        }
     }
     return e;
 }
