@@ -118,7 +118,8 @@ static void check_shape(int B, int Hq, int Hkv, int Nq, int Nk, bool causal) {
             check_prefill<false>(B, Hq, Hkv, Nq, Nk, kvg, 128, 32, 32);
             check_prefill<false>(B, Hq, Hkv, Nq, Nk, kvg, 128, 32, 64);
         }
-        check_bwd_order(B * Hkv, 1, (Nk + 127) / 128, kvg);             // dK/dV: key tiles
+        check_bwd_order(B * Hkv, 1, (Nk + 127) / 128, kvg);             // dK/dV, d = 64: 128-key tiles
+        check_bwd_order(B * Hkv, 1, (Nk + 63) / 64, kvg);               // dK/dV wave pairs, d = 128: 64-key tiles
         check_bwd_order(B * Hkv, group, (Nq + 127) / 128, kvg);         // dQ: query tiles
     }
     // backward query tiles (32 and 64 rows) and key tiles copied with clamps
