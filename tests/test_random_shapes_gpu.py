@@ -100,6 +100,9 @@ def test_random_splitkv(case):
 
 
 BWD = [c for c in _draw(10, 105400)][:6]
+# six more at d = 128, the head dimension of the wave-pair dK/dV kernel (64-key
+# blocks) and the software-pipelined dQ kernel
+BWD += [c[:5] + (128,) + c[6:] for c in _draw(6, 105500)]
 
 
 @pytest.mark.parametrize("case", BWD, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{'c' if c[6] else 'n'}"
