@@ -15,8 +15,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 LIB = os.path.join(ROOT, "exact_attention_105_amd", "libfa.so")
 
 # static LDS of the hooked kernels (bytes): d=64 prefill and dQ, d=128 prefill
-# (bf16 and fp8) and dQ, dK-only, d=64 dK/dV, dV-only, decode
-STATIC = [16384, 32768, 33792, 34816, 67584, 131072]
+# (bf16 and fp8), d=64 dK/dV, d=128 dK/dV by wave pairs, d=128 pipelined dQ,
+# decode
+STATIC = [16384, 32768, 34816, 41472, 49152, 131072]
 
 CHILD = r"""
 import ctypes, sys
