@@ -15,6 +15,14 @@
 // without raised wave priority (s_setprio 1) around the MFMA blocks, as the
 // kernel does.  Reported per SIMD: shader cycles per tile of one wave, and
 // the MFMA pipe's busy fraction, 8 MFMAs x 32 cycles x waves / cycles.
+//
+// Two more orders of the d = 128 bf16 mix over 64-key tiles (two 32-key
+// halves, 32 MFMAs per tile): "both first" issues both halves' S^T before
+// either half's softmax (the prefill kernel's order); "halves interleaved"
+// issues the second half's S^T MFMAs in one basic block with the first
+// half's softmax, and the first half's O^T MFMAs with the second half's
+// softmax (one MFMA, then seven VALU instructions, by sched_group_barrier),
+// then the second half's O^T and the next tile's first S^T.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -59,6 +67,101 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // raw scores (the kernel's threshold test), 32 exponentials, the row sum,
 // 16 v_cvt_pk_fp8_f32, and four fp8 MFMAs for O^T.
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+// Softmax of one 32-key half: exponentials, row sum into l, P as two bf16 B operands.
+__device__ __forceinline__ void softmax_half(f32x16& s, float c, float m, float& l, bf16x8& pa, bf16x8& pb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c, -m));
+    float t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t8[i] = s[2 * i] + s[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t8[i] = t8[2 * i] + t8[2 * i + 1];
+    l += (t8[0] + t8[1]) + (t8[2] + t8[3]);
+    u32x4 p0, p1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        p0[e] = pack2(s[2 * e], s[2 * e + 1]);
+        p1[e] = pack2(s[8 + 2 * e], s[8 + 2 * e + 1]);
+    }
+    pa = __builtin_bit_cast(bf16x8, p0);
+    pb = __builtin_bit_cast(bf16x8, p1);
+}
+
+// 1: d = 128, 64-key tiles, both halves' S^T first; 2: halves interleaved.
+template <int ORDER, bool PRIO>
+__global__ __launch_bounds__(256, 3) void phases64_kernel(float* out, Times* times, float seed) {
+    constexpr int KS = 8, DB = 4;
+    bf16x8 kf[KS], qf[KS];
+    for (int j = 0; j < KS; ++j)
+        for (int i = 0; i < 8; ++i) {
+            kf[j][i] = (__bf16)(seed * (threadIdx.x + i + j));
+            qf[j][i] = (__bf16)(seed * (i + 1 + j));
+        }
+    f32x16 o[DB];
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    float l = 0.f, m = 0.f;
+    const float c = 0.18f;
+    auto scores = [&](int h) {
+        f32x16 s{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[(ks + h) % KS], qf[ks], s, 0, 0, 0);
+        return s;
+    };
+    auto accumulate = [&](int h, bf16x8 pa, bf16x8 pb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[(db + h) % KS], pa, o[db], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[(db + h + 1) % KS], pb, o[db], 0, 0, 0);
+    };
+    auto interleave8 = [] {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        }
+    };
+    Times t;
+    stamp(&t, false);
+    f32x16 s0 = scores(0);
+    for (int it = 0; it < kTiles; ++it) {
+        bf16x8 p0a, p0b, p1a, p1b;
+        if constexpr (ORDER == 1) {
+            if (PRIO) __builtin_amdgcn_s_setprio(1);
+            if (it > 0) s0 = scores(0);
+            f32x16 s1 = scores(1);
+            if (PRIO) __builtin_amdgcn_s_setprio(0);
+            softmax_half(s0, c, m, l, p0a, p0b);
+            softmax_half(s1, c, m, l, p1a, p1b);
+            if (PRIO) __builtin_amdgcn_s_setprio(1);
+            accumulate(0, p0a, p0b);
+            accumulate(1, p1a, p1b);
+            if (PRIO) __builtin_amdgcn_s_setprio(0);
+        } else {
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 s1 = scores(1);
+            softmax_half(s0, c, m, l, p0a, p0b);
+            interleave8();
+            __builtin_amdgcn_sched_barrier(0);
+            accumulate(0, p0a, p0b);
+            softmax_half(s1, c, m, l, p1a, p1b);
+            interleave8();
+            __builtin_amdgcn_sched_barrier(0);
+            if (PRIO) __builtin_amdgcn_s_setprio(1);
+            accumulate(1, p1a, p1b);
+            s0 = scores(0);
+            if (PRIO) __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        m += 1e-9f * l;                         // keeps the loop from being hoisted
+    }
+    stamp(&t, true);
+    float r = l + m + s0[0];
+    for (int db = 0; db < DB; ++db)
+        for (int i = 0; i < 16; ++i) r += o[db][i];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+    if ((threadIdx.x & 63) == 0) times[blockIdx.x * 4 + (threadIdx.x >> 6)] = t;
+}
 
 template <int D, bool PRIO>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void phases_kernel(float* out, Times* times, float seed) {
@@ -163,16 +266,22 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void phases_kernel(float* out
 
 static Times h_times[256 * 8 * 4];
 
-// MFMA pipe cycles per tile and wave: 32 per bf16 32x32x16, 64 per fp8 32x32x64
+// MFMA pipe cycles per tile and wave: 32 per bf16 32x32x16, 64 per fp8 32x32x64.
+// D = 1 and 2 select phases64_kernel's orders (32 MFMAs per 64-key tile).
 template <int D>
 static void run(int cus, float* out, Times* d_times, int max_wps, const char* name) {
-    const double mfma_cycles = D == 8 ? 8 * 64.0 : 2 * (D / 16) * 32.0;
+    const double mfma_cycles = D == 8 ? 8 * 64.0 : D <= 2 ? 32 * 32.0 : 2 * (D / 16) * 32.0;
     for (int wps = 1; wps <= max_wps; ++wps)
         for (int prio = 0; prio < 2; ++prio) {
             const int nb = cus * wps;
             for (int rep = 0; rep < 2; ++rep) {
-                if (prio) hipLaunchKernelGGL((phases_kernel<D, true>), dim3(nb), dim3(256), 0, 0, out, d_times, 0.001f);
-                else hipLaunchKernelGGL((phases_kernel<D, false>), dim3(nb), dim3(256), 0, 0, out, d_times, 0.001f);
+                if constexpr (D <= 2) {
+                    if (prio) hipLaunchKernelGGL((phases64_kernel<D, true>), dim3(nb), dim3(256), 0, 0, out, d_times, 0.001f);
+                    else hipLaunchKernelGGL((phases64_kernel<D, false>), dim3(nb), dim3(256), 0, 0, out, d_times, 0.001f);
+                } else {
+                    if (prio) hipLaunchKernelGGL((phases_kernel<D, true>), dim3(nb), dim3(256), 0, 0, out, d_times, 0.001f);
+                    else hipLaunchKernelGGL((phases_kernel<D, false>), dim3(nb), dim3(256), 0, 0, out, d_times, 0.001f);
+                }
                 CHECK(hipDeviceSynchronize());
             }
             CHECK(hipMemcpy(h_times, d_times, (size_t)nb * 4 * sizeof(Times), hipMemcpyDeviceToHost));
@@ -203,6 +312,8 @@ int main() {
     printf("| tile | waves per SIMD | s_setprio around MFMAs | shader cycles per tile per wave | MFMA busy | clock MHz |\n|---|---|---|---|---|---|\n");
     run<64>(cus, out, d_times, 4, "bf16 d=64, 32 keys");
     run<128>(cus, out, d_times, 3, "bf16 d=128, 32 keys");
+    run<1>(cus, out, d_times, 3, "bf16 d=128, 64 keys, both halves' S^T first");
+    run<2>(cus, out, d_times, 3, "bf16 d=128, 64 keys, halves interleaved");
     run<8>(cus, out, d_times, 3, "fp8 d=128, 64 keys");
     CHECK(hipFree(out));
     CHECK(hipFree(d_times));
