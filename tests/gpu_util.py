@@ -75,7 +75,8 @@ def compare_bf16(o, lse, o_ref, lse_ref, what: str):
 
 # The fp8 matrix instruction (v_mfma ... f8f6f4) adds its 64 products in
 # chunks of 8, each product aligned to the largest exponent in its chunk and
-# truncated there (measured on the GPU): a score's error is at
+# truncated there (measured on the GPU by the microbenchmark
+# exact_attention_105_amd/microbench/fp8_accumulation.hip): a score's error is at
 # most FP8_MFMA_TRUNC * sum_t |q_t k_t| (the measured worst case is about half
 # of that).  A row's log-sum-exp moves by at most the largest error of its
 # scores, so the LSE bound of an FP8 row is FP8_MFMA_TRUNC * |scale| *
