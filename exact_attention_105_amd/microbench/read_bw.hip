@@ -1,6 +1,6 @@
 // How fast can a kernel stream reads from HBM on this GPU?  The decode
 // kernel reads K and V once and is bound by that rate, so its roofline
-// fraction should be judged against what plain streaming reads reach, not
+// fraction is best read against what plain streaming reads reach, not
 // only against the nameplate 8 TB/s.
 //
 // A 4 GiB buffer is read once per launch with 16-byte vector loads, U loads
