@@ -713,7 +713,7 @@ def main():
         return
     args.warmup = WARMUP if args.warmup is None else args.warmup
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the kernels and this benchmark use one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.rotate:

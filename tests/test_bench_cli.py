@@ -1,6 +1,6 @@
-"""bench.py's command-line contract that holds without a GPU: this build runs
-on one GPU, so --gpus above 1 ends with an error line and a non-zero status
-before any device work."""
+"""bench.py's command-line contract that holds without a GPU: the benchmark
+measures one GPU, so --gpus above 1 ends with an error line and a non-zero
+status before any device work."""
 import json
 import os
 import subprocess
