@@ -36,9 +36,10 @@
 //     S = Q K^T, dP = dO V^T      (A: Q / dO rows from LDS, B: K / V rows in
 //                                   registers; lane = key)
 //     dV^T += dO^T P, dK^T += Q^T dS   (A: transposing LDS reads of dO / Q)
-// Tiles are copied straight into LDS (global_load_lds_dwordx4), two stages,
-// XOR-swizzled in 16-byte units so that both the ds_read_b128 row reads and the
-// transposing reads are conflict-free (BwdCfg::swz).
+// Tiles are copied straight into LDS (global_load_lds_dwordx4), two stages
+// (three in the pipelined dQ kernel), XOR-swizzled in 16-byte units so that
+// both the ds_read_b128 row reads and the transposing reads are conflict-free
+// (BwdCfg::swz).
 #include <algorithm>
 #include <type_traits>
 
