@@ -27,20 +27,21 @@ def gpu():
     fa.load()
 
 
-def _draw(n, seed):
+def _draw(n, seed, nmax=420):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(n):
         Hkv = int(rng.choice([1, 2, 3]))
         g = int(rng.choice([1, 2, 4]))
-        Nq = int(rng.integers(1, 420))
-        Nk = int(rng.integers(1, 420)) if rng.random() < 0.7 else Nq
+        Nq = int(rng.integers(1, nmax))
+        Nk = int(rng.integers(1, nmax)) if rng.random() < 0.7 else Nq
         out.append((int(rng.integers(1, 3)), Hkv * g, Hkv, Nq, Nk, int(rng.choice([64, 128])),
                     bool(rng.random() < 0.5), float(rng.choice([1.0, -1.0, 0.5]))))
     return out
 
 
 FWD = _draw(16, 105100)
+FWD += _draw(12, 105110, 1400)       # longer rows: up to 11 query tiles and 44 key tiles
 
 
 @pytest.mark.parametrize("case", FWD, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{'c' if c[6] else 'n'}s{c[7]}"
@@ -103,6 +104,7 @@ BWD = [c for c in _draw(10, 105400)][:6]
 # six more at d = 128, the head dimension of the wave-pair dK/dV kernel (64-key
 # blocks) and the software-pipelined dQ kernel
 BWD += [c[:5] + (128,) + c[6:] for c in _draw(6, 105500)]
+BWD += [c[:5] + (128,) + c[6:] for c in _draw(6, 105510, 700)]
 
 
 @pytest.mark.parametrize("case", BWD, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{'c' if c[6] else 'n'}"
