@@ -660,15 +660,24 @@ __global__ __launch_bounds__(256, 3) void fa_bwd_dkv_pair_kernel(BwdParams pin) 
                 *reinterpret_cast<f32x4*>(px + j * 256 + lane * 4) = f32x4{pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]};
             pack_b(pv, pk);
         }
+        f32x16 sd;                               // dS wave: dP - D, ready before P arrives
+        if constexpr (DSW) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 dl = *reinterpret_cast<const f32x4*>(scratch + 8 * a + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sd[4 * a + r] = s[4 * a + r] - dl[r];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         bwd_barrier();                           // P of the tile is in LDS
         if constexpr (DSW) {
             f32x16 ds;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const f32x4 dl = *reinterpret_cast<const f32x4*>(scratch + 8 * a + 4 * g);
                 const f32x4 pv = *reinterpret_cast<const f32x4*>(px + a * 256 + lane * 4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ds[4 * a + r] = pv[r] * (s[4 * a + r] - dl[r]);
+                for (int r = 0; r < 4; ++r) ds[4 * a + r] = pv[r] * sd[4 * a + r];
             }
             pack_b(ds, pk);
         }
